@@ -1,0 +1,177 @@
+/*
+ * qlin.h -- C ABI of the MI355X (gfx950) quantized skinny linear layer.
+ *
+ * One quantized linear layer y[M,N] = dequant(quant(x)[M,K] . W_q[N,K]^T)
+ * for LLM decode at small token counts M, in the three 8-bit formats of
+ * "Building a High-Performance and Portable vLLM Linear Backend with Helion",
+ * section "Scope":
+ *   QLIN_FP8_DYNAMIC  fp8 E4M3 codes, one activation scale per token
+ *                     (computed at run time), one weight scale per output
+ *                     channel;
+ *   QLIN_W8A8_INT8    int8 codes, the same scale granularity, int32 sums;
+ *   QLIN_BLOCK_FP8    fp8 E4M3 codes, one activation scale per token and
+ *                     128-wide K group (1x128), one weight scale per 128x128
+ *                     block of W.
+ * The product is the one of section "Kernel Implementation" (out = a @ b
+ * with a wide accumulator); Standard, Split-K and Swap-AB are schedules of
+ * it that give the same result, chosen per shape and token count from an
+ * offline table (sections "Kernel Implementation" and "Per-shape Config
+ * Tuning").
+ *
+ * Numbers: fp8 is OCP E4M3FN (largest finite 448, no infinity); int8 is
+ * symmetric in [-127, 127].  A scale is amax / qmax as one fp32 division
+ * (qmax = 448 or 127); a zero run has scale 0 and all-zero codes.  A code is
+ * the fp32 quotient x / scale rounded to nearest-even and saturated.
+ *
+ * Conventions for every call:
+ *   - all tensor arguments are device pointers (hipMalloc'ed or torch CUDA
+ *     tensors), dense row-major unless a leading dimension is given, owned by
+ *     the caller; the library never allocates, frees, synchronizes or reads
+ *     device memory on the host inside these calls;
+ *   - `stream` is a hipStream_t (NULL = the default stream); work is only
+ *     enqueued on it, so every call may be captured into a hipGraph;
+ *   - arguments are validated before any HIP call; on error nothing is
+ *     enqueued and a qlin_status other than QLIN_OK is returned; nothing
+ *     aborts and nothing throws across this interface;
+ *   - device pointers must be 16-byte aligned; K must be a multiple of 16
+ *     (128 for QLIN_BLOCK_FP8, which also needs N % 128 == 0);
+ *   - activations must be finite; results for inf/NaN inputs are unspecified.
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLIN_ABI_VERSION 1
+/* Largest token count served by the tuned decode path (the pages' hybrid
+ * dispatch threshold, section "Hybrid Dispatch"). */
+#define QLIN_MAX_DECODE_M 32
+
+typedef enum {
+    QLIN_FP8_DYNAMIC = 0,
+    QLIN_W8A8_INT8 = 1,
+    QLIN_BLOCK_FP8 = 2
+} qlin_format;
+
+typedef enum {
+    QLIN_OUT_BF16 = 0,    /* y: bf16 [M,N], the product                     */
+    QLIN_OUT_F32_ACC = 1, /* y: fp32 [M,N], scaled sums before bf16 rounding */
+    QLIN_OUT_I32_ACC = 2  /* y: int32 [M,N], raw sums (W8A8_INT8 only)       */
+} qlin_out_type;
+
+typedef enum {
+    QLIN_OK = 0,
+    QLIN_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad config      */
+    QLIN_ERR_ALIGNMENT = 2,   /* pointer not 16-byte aligned or bad stride   */
+    QLIN_ERR_SHAPE = 3,       /* M, N, K out of range or not multiples       */
+    QLIN_ERR_WORKSPACE = 4,   /* workspace missing or too small              */
+    QLIN_ERR_NO_CONFIG = 5,   /* strict mode: no table entry for this shape  */
+    QLIN_ERR_TABLE = 6,       /* table file unreadable, malformed, wrong arch */
+    QLIN_ERR_HIP = 7          /* a HIP runtime call failed                   */
+} qlin_status;
+
+/* One schedule of the contraction (section "Kernel Implementation": the
+ * split_k and swap_ab tunables, plus the tile shape).
+ *   swap_ab  0: tokens fill the matrix-core row operand (Standard);
+ *            1: weight rows fill it and the result is transposed back,
+ *               y = (W_q . x_q^T)^T (Swap-AB).
+ *   split_k  number of K partitions handled by separate workgroups, 1..64;
+ *            each covers ceil(K / split_k) rounded up to 128 (the effective
+ *            count can be lower); partial sums are added in a workspace.
+ *   tile_m   tokens per tile: 16 or 32.
+ *   tile_n   output channels per workgroup: a multiple of 16, <= 256.
+ *   waves    64-lane waves per workgroup: 1, 2, 4 or 8.
+ *   k_waves  how many of those waves split the workgroup's K range
+ *            (the rest split tile_n); divides waves.                        */
+typedef struct {
+    int32_t swap_ab;
+    int32_t split_k;
+    int32_t tile_m;
+    int32_t tile_n;
+    int32_t waves;
+    int32_t k_waves;
+} qlin_config;
+
+/* Activation quantization (per token, or per token and 1x128 group for
+ * QLIN_BLOCK_FP8), the dynamic step of section "Scope".
+ *   x        bf16 [M, ldx] (row stride ldx >= K elements, ldx % 8 == 0)
+ *   xq       [M, K] codes: int8 (W8A8_INT8) or fp8 E4M3 bytes
+ *   x_scales fp32 [M], or [M][K/128] for QLIN_BLOCK_FP8
+ * M may be 0 (nothing is enqueued). */
+qlin_status qlin_quantize_act(qlin_format fmt, int M, int K, const void *x, int64_t ldx,
+                              void *xq, float *x_scales, void *stream);
+
+/* Weight quantization (offline preparation; same rules, one scale per output
+ * channel, or per 128x128 block for QLIN_BLOCK_FP8).
+ *   w        fp32 [N, K], row n = output channel n
+ *   wq       [N, K] codes
+ *   w_scales fp32 [N], or [N/128][K/128] for QLIN_BLOCK_FP8 */
+qlin_status qlin_quantize_weight(qlin_format fmt, int N, int K, const float *w, void *wq,
+                                 float *w_scales, void *stream);
+
+/* The quantized GEMM y = dequant(xq . wq^T).
+ *   xq, x_scales  as produced by qlin_quantize_act
+ *   wq, w_scales  as produced by qlin_quantize_weight ([N,K] row-major)
+ *   y             [M, N] row-major of the out_type's element type
+ *   cfg           NULL: look the schedule up with qlin_select_variant;
+ *                 otherwise that schedule is forced (it must be valid)
+ *   workspace     needed when the schedule splits K: at least
+ *                 qlin_workspace_bytes(...) bytes, zero-filled before its
+ *                 first use; every call leaves it zero again.  Calls that
+ *                 overlap in time must not share a workspace.
+ * Returns QLIN_ERR_NO_CONFIG in strict mode when cfg is NULL and the table
+ * has no entry for (fmt, N, K, bucket(M)). */
+qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq,
+                      const float *x_scales, const void *wq, const float *w_scales, void *y,
+                      qlin_out_type out_type, const qlin_config *cfg, void *workspace,
+                      size_t ws_bytes, void *stream);
+
+/* Schedule lookup (host only, no device work).  M rounds up to the next
+ * tuned token bucket {1,2,4,8,16,24,32} (section "Per-shape Config Tuning"),
+ * or {64,128,256,512} above 32.  In strict mode a missing entry is
+ * QLIN_ERR_NO_CONFIG (the opt-in rule that start-up fails without tuned
+ * configurations); in permissive mode a built-in rule answers. */
+qlin_status qlin_select_variant(qlin_format fmt, int M, int N, int K, qlin_config *out);
+
+/* Workspace bytes qlin_gemm needs for this schedule (0 when split_k is 1).
+ * cfg NULL: for the schedule qlin_select_variant picks. */
+qlin_status qlin_workspace_bytes(qlin_format fmt, int M, int N, int K, const qlin_config *cfg,
+                                 size_t *bytes);
+
+/* Checks a schedule against (fmt, M, N, K) without launching anything. */
+qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qlin_config *cfg);
+
+/* Selection table.  qlin_load_table parses a text table (replacing any loaded
+ * one; path NULL = the table installed next to the library); the table is
+ * immutable afterwards, so lookups are thread-safe.  qlin_set_strict(1)
+ * makes a missing entry an error (the default is 0, permissive). */
+qlin_status qlin_load_table(const char *path);
+qlin_status qlin_set_strict(int strict);
+int qlin_table_entries(void);
+
+/* hipGraph capture of a decode step (section "Hybrid Dispatch": the tuned
+ * path runs only under graph replay).  qlin_graph_begin starts capturing
+ * `stream` (not the NULL stream); every qlin call on it until
+ * qlin_graph_end is recorded instead of run; qlin_graph_end instantiates
+ * the graph into *graph.  qlin_graph_launch replays it on a stream. */
+typedef struct qlin_graph_s *qlin_graph;
+qlin_status qlin_graph_begin(void *stream);
+qlin_status qlin_graph_end(void *stream, qlin_graph *graph);
+qlin_status qlin_graph_launch(qlin_graph graph, void *stream);
+qlin_status qlin_graph_destroy(qlin_graph graph);
+
+/* Helpers. */
+const char *qlin_status_str(qlin_status st);
+int qlin_abi_version(void);
+/* Last HIP error code seen by a call that returned QLIN_ERR_HIP (0 if none). */
+int qlin_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

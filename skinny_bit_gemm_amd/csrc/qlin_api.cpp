@@ -1,0 +1,272 @@
+// qlin_api.cpp -- the C ABI: argument validation, schedule planning and
+// dispatch to the gfx950 kernels.  Every check runs before the first HIP
+// call, so a rejected call touches neither the device nor the stream.
+#include <cstdint>
+#include <cstdio>
+#include <new>
+
+#include <hip/hip_runtime_api.h>
+
+#include "qlin_internal.h"
+
+namespace qlin {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool fmt_ok(int fmt) { return fmt == QLIN_FP8_DYNAMIC || fmt == QLIN_W8A8_INT8 || fmt == QLIN_BLOCK_FP8; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// int32 sums of int8 products stay exact while 127 * 127 * K < 2^31
+constexpr int kMaxKInt8 = 133120;
+constexpr int kMaxDim = 1 << 20;
+
+qlin_status shape_ok(int fmt, int M, int N, int K) {
+    if (M < 0 || M > kMaxDim || N < 16 || N > kMaxDim || K < 16 || K > kMaxDim) return QLIN_ERR_SHAPE;
+    if (N % 16 != 0 || K % 16 != 0) return QLIN_ERR_SHAPE;
+    if (fmt == QLIN_BLOCK_FP8 && (N % kGroup != 0 || K % kGroup != 0)) return QLIN_ERR_SHAPE;
+    if (fmt == QLIN_W8A8_INT8 && K > kMaxKInt8) return QLIN_ERR_SHAPE;
+    return QLIN_OK;
+}
+
+qlin_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return QLIN_OK;
+    g_last_hip_error = (int)e;
+    return QLIN_ERR_HIP;
+}
+
+qlin_status resolve_config(qlin_format fmt, int M, int N, int K, const qlin_config *cfg,
+                           qlin_config *out) {
+    if (cfg) {
+        *out = *cfg;
+        return QLIN_OK;
+    }
+    bool found = false;
+    qlin_status st = table_lookup(fmt, M, N, K, out, &found);
+    if (st != QLIN_OK) return st;
+    if (found) return QLIN_OK;
+    if (strict_mode()) return QLIN_ERR_NO_CONFIG;
+    default_config(fmt, M, N, K, out);
+    return QLIN_OK;
+}
+
+}  // namespace
+
+qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c, Plan *p) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    if (M < 1) M = 1;
+    if (c.swap_ab != 0 && c.swap_ab != 1) return QLIN_ERR_INVALID_ARG;
+    if (c.split_k < 1 || c.split_k > kMaxSplit) return QLIN_ERR_INVALID_ARG;
+    if (c.tile_m != 16 && c.tile_m != 32) return QLIN_ERR_INVALID_ARG;
+    if (c.waves != 1 && c.waves != 2 && c.waves != 4 && c.waves != 8) return QLIN_ERR_INVALID_ARG;
+    if (c.k_waves < 1 || c.k_waves > c.waves || c.waves % c.k_waves != 0) return QLIN_ERR_INVALID_ARG;
+    const int nw = c.waves / c.k_waves;
+    if (c.tile_n < 16 || c.tile_n > 256 || c.tile_n % (16 * nw) != 0) return QLIN_ERR_INVALID_ARG;
+    const int nr = c.tile_n / (16 * nw);
+    if (!gemm_variant_exists(fmt, c.tile_m, nr)) return QLIN_ERR_INVALID_ARG;
+    const int mt = c.tile_m / 16;
+    p->tile_m = c.tile_m;
+    p->tile_n = c.tile_n;
+    p->nr = nr;
+    p->nw = nw;
+    p->kw = c.k_waves;
+    p->waves = c.waves;
+    p->nkb = (K + kGroup - 1) / kGroup;
+    p->kb_per_split = (p->nkb + c.split_k - 1) / c.split_k;
+    p->nsplit = (p->nkb + p->kb_per_split - 1) / p->kb_per_split;
+    // activation codes (2 KB per 16 tokens and K block) plus, for the block
+    // format, one fp32 scale per token and K block
+    const int per_block = mt * 2048 + (fmt == QLIN_BLOCK_FP8 ? mt * 16 * 4 : 0);
+    int pb = kLdsBudget / per_block;
+    if (pb > p->kb_per_split) pb = p->kb_per_split;
+    p->phase_blocks = pb;
+    size_t lds = (size_t)pb * per_block;
+    const size_t red = (size_t)(c.k_waves - 1) * nw * nr * mt * 64 * 16;
+    if (red > lds) lds = red;
+    p->lds_bytes = lds;
+    p->n_tiles = (N + c.tile_n - 1) / c.tile_n;
+    p->m_tiles = (M + c.tile_m - 1) / c.tile_m;
+    if (p->nsplit > 1) {
+        p->ws_acc_bytes = align256((size_t)M * N * 4);
+        p->ws_bytes = p->ws_acc_bytes + align256((size_t)p->n_tiles * p->m_tiles * 4);
+    } else {
+        p->ws_acc_bytes = 0;
+        p->ws_bytes = 0;
+    }
+    return QLIN_OK;
+}
+
+}  // namespace qlin
+
+using namespace qlin;
+
+extern "C" {
+
+qlin_status qlin_quantize_act(qlin_format fmt, int M, int K, const void *x, int64_t ldx, void *xq,
+                              float *x_scales, void *stream) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    if (M < 0 || M > kMaxDim || K < 16 || K > kMaxDim || K % 16 != 0) return QLIN_ERR_SHAPE;
+    if (fmt == QLIN_BLOCK_FP8 && K % kGroup != 0) return QLIN_ERR_SHAPE;
+    if (ldx < K || ldx % 8 != 0) return QLIN_ERR_ALIGNMENT;
+    if (!x || !xq || !x_scales) return QLIN_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scales)) return QLIN_ERR_ALIGNMENT;
+    if (M == 0) return QLIN_OK;
+    return hip_status(launch_quant_act(fmt, M, K, x, ldx, xq, x_scales,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+qlin_status qlin_quantize_weight(qlin_format fmt, int N, int K, const float *w, void *wq,
+                                 float *w_scales, void *stream) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    qlin_status st = shape_ok(fmt, 1, N, K);
+    if (st != QLIN_OK) return st;
+    if (!w || !wq || !w_scales) return QLIN_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(wq) || !aligned4(w_scales)) return QLIN_ERR_ALIGNMENT;
+    return hip_status(launch_quant_weight(fmt, N, K, w, wq, w_scales,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qlin_config *cfg) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    qlin_status st = shape_ok(fmt, M, N, K);
+    if (st != QLIN_OK) return st;
+    if (!cfg) return QLIN_ERR_INVALID_ARG;
+    Plan p;
+    return make_plan(fmt, M, N, K, *cfg, &p);
+}
+
+qlin_status qlin_select_variant(qlin_format fmt, int M, int N, int K, qlin_config *out) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    if (!out) return QLIN_ERR_INVALID_ARG;
+    qlin_status st = shape_ok(fmt, M, N, K);
+    if (st != QLIN_OK) return st;
+    return resolve_config(fmt, M, N, K, nullptr, out);
+}
+
+qlin_status qlin_workspace_bytes(qlin_format fmt, int M, int N, int K, const qlin_config *cfg,
+                                 size_t *bytes) {
+    if (!fmt_ok(fmt) || !bytes) return QLIN_ERR_INVALID_ARG;
+    qlin_status st = shape_ok(fmt, M, N, K);
+    if (st != QLIN_OK) return st;
+    qlin_config c;
+    st = resolve_config(fmt, M, N, K, cfg, &c);
+    if (st != QLIN_OK) return st;
+    Plan p;
+    st = make_plan(fmt, M, N, K, c, &p);
+    if (st != QLIN_OK) return st;
+    *bytes = p.ws_bytes;
+    return QLIN_OK;
+}
+
+qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, const float *x_scales,
+                      const void *wq, const float *w_scales, void *y, qlin_out_type out_type,
+                      const qlin_config *cfg, void *workspace, size_t ws_bytes, void *stream) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    if (out_type != QLIN_OUT_BF16 && out_type != QLIN_OUT_F32_ACC && out_type != QLIN_OUT_I32_ACC)
+        return QLIN_ERR_INVALID_ARG;
+    if (out_type == QLIN_OUT_I32_ACC && fmt != QLIN_W8A8_INT8) return QLIN_ERR_INVALID_ARG;
+    qlin_status st = shape_ok(fmt, M, N, K);
+    if (st != QLIN_OK) return st;
+    if (!xq || !x_scales || !wq || !w_scales || !y) return QLIN_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(x_scales) ||
+        !aligned4(w_scales))
+        return QLIN_ERR_ALIGNMENT;
+    qlin_config c;
+    st = resolve_config(fmt, M, N, K, cfg, &c);
+    if (st != QLIN_OK) return st;
+    Plan p;
+    st = make_plan(fmt, M, N, K, c, &p);
+    if (st != QLIN_OK) return st;
+    if (p.ws_bytes > 0) {
+        if (!workspace || ws_bytes < p.ws_bytes) return QLIN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return QLIN_ERR_ALIGNMENT;
+    }
+    if (M == 0) return QLIN_OK;
+
+    GemmLaunch g;
+    g.xq = static_cast<const uint8_t *>(xq);
+    g.xs = x_scales;
+    g.wq = static_cast<const uint8_t *>(wq);
+    g.wsc = w_scales;
+    g.y = y;
+    g.acc_ws = p.ws_bytes ? workspace : nullptr;
+    g.counters = p.ws_bytes ? reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + p.ws_acc_bytes)
+                            : nullptr;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.nkb = p.nkb;
+    g.kb_per_split = p.kb_per_split;
+    g.nsplit = p.nsplit;
+    g.phase_blocks = p.phase_blocks;
+    g.out_type = out_type;
+    g.n_tiles = p.n_tiles;
+    g.m_tiles = p.m_tiles;
+    g.nw = p.nw;
+    g.kw = p.kw;
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, g, p.lds_bytes,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+struct qlin_graph_s {
+    hipGraphExec_t exec;
+};
+
+qlin_status qlin_graph_begin(void *stream) {
+    if (!stream) return QLIN_ERR_INVALID_ARG;
+    return hip_status(hipStreamBeginCapture(static_cast<hipStream_t>(stream),
+                                            hipStreamCaptureModeThreadLocal));
+}
+
+qlin_status qlin_graph_end(void *stream, qlin_graph *graph) {
+    if (!stream || !graph) return QLIN_ERR_INVALID_ARG;
+    hipGraph_t g = nullptr;
+    qlin_status st = hip_status(hipStreamEndCapture(static_cast<hipStream_t>(stream), &g));
+    if (st != QLIN_OK) return st;
+    hipGraphExec_t exec = nullptr;
+    st = hip_status(hipGraphInstantiate(&exec, g, nullptr, nullptr, 0));
+    hipGraphDestroy(g);
+    if (st != QLIN_OK) return st;
+    qlin_graph h = new (std::nothrow) qlin_graph_s;
+    if (!h) {
+        hipGraphExecDestroy(exec);
+        return QLIN_ERR_INVALID_ARG;
+    }
+    h->exec = exec;
+    *graph = h;
+    return QLIN_OK;
+}
+
+qlin_status qlin_graph_launch(qlin_graph graph, void *stream) {
+    if (!graph) return QLIN_ERR_INVALID_ARG;
+    return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)));
+}
+
+qlin_status qlin_graph_destroy(qlin_graph graph) {
+    if (!graph) return QLIN_ERR_INVALID_ARG;
+    qlin_status st = hip_status(hipGraphExecDestroy(graph->exec));
+    delete graph;
+    return st;
+}
+
+const char *qlin_status_str(qlin_status st) {
+    switch (st) {
+    case QLIN_OK: return "ok";
+    case QLIN_ERR_INVALID_ARG: return "invalid argument";
+    case QLIN_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case QLIN_ERR_SHAPE: return "unsupported shape";
+    case QLIN_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLIN_ERR_NO_CONFIG: return "no tuned configuration for this shape (strict mode)";
+    case QLIN_ERR_TABLE: return "selection table unreadable or malformed";
+    case QLIN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int qlin_abi_version(void) { return QLIN_ABI_VERSION; }
+
+int qlin_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// qlin_internal.h -- declarations shared by the library's host and device
+// sources (not part of the public ABI).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/qlin.h"
+
+namespace qlin {
+
+constexpr int kGroup = 128;          // K block: one fp8 MFMA, one 1x128 scale group
+constexpr int kMaxWaves = 8;         // waves per workgroup
+constexpr int kLdsBudget = 64 * 1024; // bytes of LDS a GEMM workgroup may use
+constexpr int kMaxSplit = 64;
+
+// Everything a GEMM launch needs, resolved on the host.
+struct GemmLaunch {
+    const uint8_t *xq;
+    const float *xs;
+    const uint8_t *wq;
+    const float *wsc;
+    void *y;
+    void *acc_ws;        // split-K partial sums [M][N] (int32 or fp32), zero between calls
+    uint32_t *counters;  // split-K arrival counters, one per output tile, zero between calls
+    int M, N, K;
+    int nkb;             // K blocks of 128 (last one may be partial)
+    int kb_per_split;    // K blocks per split-K partition
+    int nsplit;          // effective number of partitions (grid z)
+    int phase_blocks;    // K blocks of activations staged in LDS at once
+    int out_type;
+    int n_tiles, m_tiles;
+    int nw, kw;          // waves along N and along K
+};
+
+// Derived launch geometry for (fmt, M, N, K, cfg).
+struct Plan {
+    int tile_m, tile_n, nr, nw, kw, waves;
+    int nkb, kb_per_split, nsplit, phase_blocks;
+    int n_tiles, m_tiles;
+    size_t lds_bytes;
+    size_t ws_bytes;      // workspace bytes (0 without split)
+    size_t ws_acc_bytes;  // of which partial sums
+};
+
+// Fills *plan; returns QLIN_OK or the reason the schedule is invalid.
+qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &cfg, Plan *plan);
+
+// Host-side selection table (qlin_table.cpp).
+qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out, bool *found);
+void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out);
+int token_bucket(int M);
+bool strict_mode();
+
+// Kernel launchers (qlin_kernels.hip); they only enqueue.
+hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, void *xq,
+                            float *xs, hipStream_t s);
+hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, float *ws,
+                               hipStream_t s);
+hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, const GemmLaunch &g,
+                       size_t lds_bytes, hipStream_t s);
+bool gemm_variant_exists(int fmt, int tile_m, int nr);
+
+}  // namespace qlin

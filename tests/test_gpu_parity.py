@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: quantized codes and fp32 scales bit-exact; int8 int32 accumulators
+bit-exact for every schedule; bf16 outputs within
+|y - ref| <= 1e-2 |ref| + 1e-3 max|ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import skinny_bit_gemm_amd as q
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+from _gpu import (as_u8, gpu_gemm, gpu_quant_act, gpu_quant_weight, workspace_for,  # noqa: E402
+                  y_to_numpy)
+
+FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
+FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.lib()
+    oracle.build()
+
+
+def cfg(swap=0, split=1, tile_m=16, tile_n=32, waves=4, k_waves=4):
+    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves)
+
+
+# schedules every format is checked with: Standard, Swap-AB, Split-K (with
+# and without Swap-AB), several tile shapes and wave arrangements
+SCHEDULES = {
+    "std": cfg(0, 1, 16, 32, 4, 4),
+    "swap": cfg(1, 1, 16, 32, 4, 4),
+    "std_m32": cfg(0, 1, 32, 32, 4, 4),
+    "swap_m32": cfg(1, 1, 32, 64, 4, 2),
+    "splitk2": cfg(0, 2, 16, 32, 4, 4),
+    "splitk4_swap": cfg(1, 4, 16, 64, 4, 1),
+    "splitk16": cfg(1, 16, 32, 16, 2, 2),
+    "nw4": cfg(0, 3, 16, 128, 8, 2),
+    "nr4": cfg(1, 2, 32, 64, 1, 1),
+    "w8k8": cfg(0, 1, 16, 16, 8, 8),
+}
+
+
+def _flush():
+    import sys
+    sys.stdout.flush()
+
+
+def check_linear(fmt, M, N, K, x, w, sched, tag=""):
+    print(f"[case] fmt={fmt} M={M} N={N} K={K} sched={sched} {tag}", flush=True)
+    qw_o, sw_o = oracle.quant_weight(fmt, w)
+    qa_o, sa_o, ref = oracle.linear(fmt, x, qw_o, sw_o)
+    wq, ws = gpu_quant_weight(fmt, w)
+    assert np.array_equal(as_u8(wq), qw_o), "weight codes differ"
+    assert np.array_equal(ws.cpu().numpy().view(np.uint32), sw_o.view(np.uint32)), "weight scales differ"
+    xq, xs = gpu_quant_act(fmt, x)
+    assert np.array_equal(as_u8(xq), qa_o), "activation codes differ"
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa_o.view(np.uint32)), "activation scales differ"
+    c = SCHEDULES[sched] if isinstance(sched, str) else sched
+    y = y_to_numpy(gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c))
+    ok, worst = oracle.tolerance_ok(y, ref)
+    assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
+    if fmt == wl.W8A8_INT8:
+        _, acc = oracle.gemm(fmt, qa_o, sa_o, qw_o, sw_o, want_acc=True)
+        yi = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, out_type=q.QLIN_OUT_I32_ACC).cpu().numpy()
+        assert np.array_equal(yi, acc), "int32 accumulators differ"
+    return y, ref
+
+
+def test_tiny_w8a8_int8_all_schedules():
+    """The tiny int8 linear (M=4, K=512, N=1024, seed 0) under every schedule."""
+    x, w = wl.tiny_case()
+    for name in SCHEDULES:
+        check_linear(wl.W8A8_INT8, 4, 1024, 512, x, w, name, "tiny")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("sched", list(SCHEDULES))
+def test_schedules_match_oracle(fmt, sched):
+    M, N, K = 7, 512, 1024
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 31)
+    check_linear(fmt, M, N, K, x, w, sched)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 24, 31, 32])
+def test_token_counts(fmt, M):
+    N, K = 384, 1280
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 40 + M)
+    for sched in ("swap", "std_m32", "splitk4_swap"):
+        check_linear(fmt, M, N, K, x, w, sched)
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
+@pytest.mark.parametrize("K", [16, 48, 1040, 2064])
+def test_ragged_k(fmt, K):
+    """K not a multiple of 128 (per-channel formats): the last block is partial."""
+    M, N = 5, 256
+    x = wl.random_bf16((M, K), K)
+    w = wl.random_weights(N, K, K + 1)
+    for sched in ("std", "swap", "splitk2", "splitk16", "nw4"):
+        check_linear(fmt, M, N, K, x, w, sched, "ragged K")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_ragged_n_tiles(fmt):
+    """N not a multiple of tile_n: the last workgroup has empty sub-tiles."""
+    M, N, K = 3, 384, 512
+    x = wl.random_bf16((M, K), 5)
+    w = wl.random_weights(N, K, 6)
+    check_linear(fmt, M, N, K, x, w, cfg(1, 2, 16, 256, 4, 1))
+    check_linear(fmt, M, N, K, x, w, cfg(0, 1, 16, 256, 8, 2))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("M", [33, 64, 100])
+def test_large_m(fmt, M):
+    N, K = 256, 1024
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 77)
+    check_linear(fmt, M, N, K, x, w, "std_m32")
+    check_linear(fmt, M, N, K, x, w, "splitk4_swap")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_default_selection_matches(fmt):
+    M, N, K = 9, 512, 2048
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 8)
+    c = q.qlin_select_variant(fmt, M, N, K)
+    check_linear(fmt, M, N, K, x, w, c, "selected")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_zero_and_outlier_rows(fmt):
+    """A zero token (scale 0, exact +0 output), a zero weight channel and a
+    token whose amax sits in an outlier group."""
+    M, N, K = 4, 256, 512
+    x = wl.activations(fmt, N, K, M).copy()
+    x[1, :] = 0
+    w = wl.random_weights(N, K, 3)
+    w[:128 if fmt == wl.BLOCK_FP8 else 1, :] = 0.0
+    y, ref = check_linear(fmt, M, N, K, x, w, "swap")
+    assert np.all(y[1] == 0) and not np.any(np.signbit(y[1]))
+    assert np.all(y[:, 0] == 0)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_quant_act_strided_and_every_bf16(fmt):
+    """Row stride ldx > K, and a sweep over every finite bf16 value."""
+    x = wl.activations(fmt, 128, 1024, 6)
+    qa_o, sa_o = oracle.quant_act(fmt, x)
+    xq, xs = gpu_quant_act(fmt, x, ldx=1024 + 64)
+    assert np.array_equal(as_u8(xq), qa_o)
+    assert np.array_equal(xs.cpu().numpy(), sa_o)
+    # every finite bf16 bit pattern, grouped in rows of 1024
+    bits = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    fin = np.isfinite(wl.bf16_bits_to_f32(bits))
+    allv = bits[fin]
+    allv = allv[: (allv.size // 1024) * 1024].reshape(-1, 1024)
+    qa_o, sa_o = oracle.quant_act(fmt, allv)
+    xq, xs = gpu_quant_act(fmt, allv)
+    assert np.array_equal(as_u8(xq), qa_o)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
+
+
+def test_e4m3_conversion_exhaustive_at_unit_scale():
+    """Rows whose amax is 448 have scale exactly 1, so the codes are the plain
+    fp32 -> E4M3 conversion of every bf16 magnitude up to 448 (and 0x80)."""
+    bits = np.arange(0, 0x43E1, dtype=np.uint16)   # +0 .. 448 in bf16
+    vals = np.concatenate([bits, bits | np.uint16(0x8000)])
+    pad = (-vals.size) % 1023
+    vals = np.concatenate([vals, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 1023)
+    rows = np.concatenate([vals, np.full((vals.shape[0], 1), 0x43E0, dtype=np.uint16)], axis=1)
+    K = 1024
+    assert rows.shape[1] == K
+    qa_o, sa_o = oracle.quant_act(wl.FP8_DYNAMIC, rows)
+    assert np.all(sa_o == 1.0)
+    xq, xs = gpu_quant_act(wl.FP8_DYNAMIC, rows)
+    assert np.array_equal(as_u8(xq), qa_o)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_splitk_workspace_left_zero_and_reusable(fmt):
+    M, N, K = 5, 512, 2048
+    c = cfg(1, 8, 16, 32, 4, 2)
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 12)
+    wq, ws = gpu_quant_weight(fmt, w)
+    xq, xs = gpu_quant_act(fmt, x)
+    work = workspace_for(fmt, M, N, K, c)
+    y1 = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, workspace=work)
+    assert int(work.count_nonzero()) == 0
+    y2 = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, workspace=work)
+    assert int(work.count_nonzero()) == 0
+    if fmt == wl.W8A8_INT8:
+        assert torch.equal(y1, y2)
+
+
+def test_int8_splitk_deterministic_accumulators():
+    M, N, K = 32, 1024, 4096
+    fmt = wl.W8A8_INT8
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 13)
+    wq, ws = gpu_quant_weight(fmt, w)
+    xq, xs = gpu_quant_act(fmt, x)
+    c = cfg(1, 16, 32, 32, 4, 4)
+    work = workspace_for(fmt, M, N, K, c)
+    first = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, q.QLIN_OUT_I32_ACC, work)
+    for _ in range(20):
+        again = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, q.QLIN_OUT_I32_ACC, work)
+        assert torch.equal(first, again)
+
+
+def test_zero_tokens_is_a_no_op():
+    fmt = wl.W8A8_INT8
+    w = wl.random_weights(256, 512, 1)
+    wq, ws = gpu_quant_weight(fmt, w)
+    xq = torch.empty((1, 512), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((1,), dtype=torch.float32, device="cuda")
+    y = torch.full((1, 256), 7, dtype=torch.int16, device="cuda")
+    assert q.qlin_gemm(fmt, 0, 256, 512, xq, xs, wq, ws, y) == 0
+    assert q.qlin_quantize_act(fmt, 0, 512, y, 512, xq, xs) == 0
+    torch.cuda.synchronize()
+    assert int((y == 7).sum()) == 256
