@@ -72,6 +72,11 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m skinny_bit_gemm_amd.build` (no CPU fallback exists)")
+        # torch ships its own HIP runtime (soname libamdhip64.so.7).  Loading
+        # torch first makes the dynamic loader bind the library to that same
+        # runtime; loading the library first would map the system runtime as
+        # a second copy, and torch's streams would be foreign handles to it.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.qlin_quantize_act.argtypes = [_I, _I, _I, _P, _I64, _P, _P, _P]
         L.qlin_quantize_weight.argtypes = [_I, _I, _I, _P, _P, _P, _P]

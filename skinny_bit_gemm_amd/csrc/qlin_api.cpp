@@ -76,9 +76,10 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     p->nkb = (K + kGroup - 1) / kGroup;
     p->kb_per_split = (p->nkb + c.split_k - 1) / c.split_k;
     p->nsplit = (p->nkb + p->kb_per_split - 1) / p->kb_per_split;
-    // activation codes (2 KB per 16 tokens and K block) plus, for the block
-    // format, one fp32 scale per token and K block
-    const int per_block = mt * 2048 + (fmt == QLIN_BLOCK_FP8 ? mt * 16 * 4 : 0);
+    // activation codes of the tile's existing token rows (128 bytes per row
+    // and K block) plus, for the block format, one fp32 scale per row and block
+    const int rows = M < c.tile_m ? M : c.tile_m;
+    const int per_block = rows * kGroup + (fmt == QLIN_BLOCK_FP8 ? rows * 4 : 0);
     int pb = kLdsBudget / per_block;
     if (pb > p->kb_per_split) pb = p->kb_per_split;
     p->phase_blocks = pb;

@@ -76,44 +76,76 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // --------------------------------------------------- activation quantization
 
-// One workgroup per token: pass 1 finds the row's amax, pass 2 writes codes.
-// Each thread handles 8 bf16 (16 bytes) at a time.
+// bf16 x 8 (one 16-byte chunk) -> max |value|
+__device__ __forceinline__ float absmax8(uint4 v) {
+    return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                       fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
+                 fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
+                       fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+}
+
+// bf16 x 8 -> 8 codes packed little-endian into two words
 template <int FMT>
-__global__ __launch_bounds__(256) void quant_token_kernel(const uint16_t *__restrict__ x,
-                                                          int64_t ldx, int K,
-                                                          uint8_t *__restrict__ xq,
-                                                          float *__restrict__ xs) {
-    __shared__ float red[4];
+__device__ __forceinline__ uint2 quant8(uint4 v, float s) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        lo |= quant_code<FMT>(bf16_lo(w[j]), s) << (16 * j);
+        lo |= quant_code<FMT>(bf16_hi(w[j]), s) << (16 * j + 8);
+        hi |= quant_code<FMT>(bf16_lo(w[j + 2]), s) << (16 * j);
+        hi |= quant_code<FMT>(bf16_hi(w[j + 2]), s) << (16 * j + 8);
+    }
+    return make_uint2(lo, hi);
+}
+
+constexpr int kQuantThreads = 512;
+
+// One workgroup per token.  With CPT > 0 every thread keeps its (at most
+// CPT) 16-byte chunks of the row in registers: one read of the row, the
+// row's amax by a wave reduction and one across waves, then the codes.
+// CPT == 0 is the fallback for very long rows: the row is read twice.
+template <int FMT, int CPT>
+__global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(const uint16_t *__restrict__ x,
+                                                                    int64_t ldx, int K,
+                                                                    uint8_t *__restrict__ xq,
+                                                                    float *__restrict__ xs) {
+    __shared__ float red[kQuantThreads / 64];
     const int m = blockIdx.x;
     const uint16_t *row = x + (int64_t)m * ldx;
+    uint8_t *qrow = xq + (int64_t)m * K;
     const int nch = K >> 3;
     float amax = 0.0f;
-    for (int c = threadIdx.x; c < nch; c += 256) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(row + c * 8);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
-                                 fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
-                                 fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+    uint4 v[CPT > 0 ? CPT : 1];
+    if constexpr (CPT > 0) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = threadIdx.x + j * kQuantThreads;
+            v[j] = c < nch ? *reinterpret_cast<const uint4 *>(row + c * 8) : make_uint4(0, 0, 0, 0);
+            amax = fmaxf(amax, absmax8(v[j]));
+        }
+    } else {
+        for (int c = threadIdx.x; c < nch; c += kQuantThreads)
+            amax = fmaxf(amax, absmax8(*reinterpret_cast<const uint4 *>(row + c * 8)));
     }
     amax = wave_max(amax);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    amax = red[0];
+#pragma unroll
+    for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
     const float s = amax == 0.0f ? 0.0f : amax / qmax_of<FMT>();
     if (threadIdx.x == 0) xs[m] = s;
-    uint8_t *qrow = xq + (int64_t)m * K;
-    for (int c = threadIdx.x; c < nch; c += 256) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(row + c * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t lo = 0, hi = 0;
+    if constexpr (CPT > 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            lo |= quant_code<FMT>(bf16_lo(w[j]), s) << (16 * j);
-            lo |= quant_code<FMT>(bf16_hi(w[j]), s) << (16 * j + 8);
-            hi |= quant_code<FMT>(bf16_lo(w[j + 2]), s) << (16 * j);
-            hi |= quant_code<FMT>(bf16_hi(w[j + 2]), s) << (16 * j + 8);
+        for (int j = 0; j < CPT; ++j) {
+            const int c = threadIdx.x + j * kQuantThreads;
+            if (c < nch) *reinterpret_cast<uint2 *>(qrow + c * 8) = quant8<FMT>(v[j], s);
         }
-        *reinterpret_cast<uint2 *>(qrow + c * 8) = make_uint2(lo, hi);
+    } else {
+        for (int c = threadIdx.x; c < nch; c += kQuantThreads)
+            *reinterpret_cast<uint2 *>(qrow + c * 8) =
+                quant8<FMT>(*reinterpret_cast<const uint4 *>(row + c * 8), s);
     }
 }
 
@@ -131,25 +163,13 @@ __global__ __launch_bounds__(256) void quant_group_kernel(const uint16_t *__rest
     const int g = live ? gi - m * G : 0;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (live) v = *reinterpret_cast<const uint4 *>(x + (int64_t)m * ldx + g * kGroup + j * 8);
-    float amax = fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
-                             fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
-                       fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
-                             fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+    float amax = absmax8(v);
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
     const float s = amax == 0.0f ? 0.0f : amax / 448.0f;
     if (!live) return;
     if (j == 0) xs[(int64_t)m * G + g] = s;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        lo |= quant_code<FMT_BLOCK>(bf16_lo(w[t]), s) << (16 * t);
-        lo |= quant_code<FMT_BLOCK>(bf16_hi(w[t]), s) << (16 * t + 8);
-        hi |= quant_code<FMT_BLOCK>(bf16_lo(w[t + 2]), s) << (16 * t);
-        hi |= quant_code<FMT_BLOCK>(bf16_hi(w[t + 2]), s) << (16 * t + 8);
-    }
-    *reinterpret_cast<uint2 *>(xq + (int64_t)m * K + g * kGroup + j * 8) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2 *>(xq + (int64_t)m * K + g * kGroup + j * 8) = quant8<FMT_BLOCK>(v, s);
 }
 
 // ------------------------------------------------------- weight quantization
@@ -219,7 +239,7 @@ __global__ __launch_bounds__(256) void quant_block_weight_kernel(const float *__
 
 // ------------------------------------------------------------------- GEMM
 //
-// Work decomposition.  A workgroup owns a tile of TM = 16*MT tokens by
+// Work decomposition.  A workgroup owns a tile of up to TM = 16*MT tokens by
 // TN = 16*NR*nw output channels and a range of 128-wide K blocks (all of K,
 // or one Split-K partition).  Its waves form an nw x kw grid: a wave owns NR
 // sub-tiles of 16 channels and every kw-th K block of the range, so the kw
@@ -235,11 +255,18 @@ __global__ __launch_bounds__(256) void quant_block_weight_kernel(const float *__
 // 16x16x128 MFMA per block (32 bytes per lane); int8 uses two 16x16x64 MFMAs
 // (bytes 0..15, then 16..31 of each lane's 32).
 //
-// Each weight lane load covers 32 contiguous bytes; the 4 lanes of a row
-// cover the row's whole 128-byte block, so a wave-wide load reads 16 full
-// 128-byte lines.  Activations for the workgroup's K range are staged once
-// in LDS in fragment order ([M sub-tile][K block][half][lane][16 bytes]), so
-// the per-block LDS reads are two conflict-free ds_read_b128.
+// Weight stream.  Each weight lane load covers 32 contiguous bytes; the 4
+// lanes of a row cover the row's whole 128-byte block, so a wave-wide load
+// reads 16 full 128-byte lines.  A wave keeps PF blocks of loads in flight
+// (a ring of PF register slots), and its first PF blocks are requested
+// before the activations are staged, so the two latencies overlap.
+//
+// Activations.  The workgroup's token rows for its K range are staged once
+// in LDS, only the rows that exist (R = min(TM, M - m0)), laid out as
+// [K block][half][quarter][row][16 bytes]: the 16 lanes of a quarter read 16
+// consecutive 16-byte chunks, so the two ds_read_b128 per block are free of
+// bank conflicts.  Lanes whose row is past R use zeros.  When R x (K range)
+// does not fit the LDS budget the range is processed in phases.
 //
 // Standard: A = activations (tokens are the MFMA rows), B = weights.  The
 // 16x16 result lane l holds column l % 16 = channel and rows 4(l/16)+i =
@@ -289,7 +316,8 @@ __device__ __forceinline__ typename AccT<FMT>::type block_mma(v8i a, v8i b,
     }
 }
 
-// 32 bytes of one weight row at byte offset k (16-byte halves beyond K read 0)
+// 32 bytes of one weight row starting at byte k of the row (p points there);
+// 16-byte halves at or beyond K read as zero
 __device__ __forceinline__ v8i load_w(const uint8_t *p, int k, int K, bool full) {
     if (full) {
         const uint4 lo = *reinterpret_cast<const uint4 *>(p);
@@ -302,7 +330,19 @@ __device__ __forceinline__ v8i load_w(const uint8_t *p, int k, int K, bool full)
     return join(lo, hi);
 }
 
-template <int FMT, bool SWAP, int MT, int NR>
+// Orders this thread's earlier global atomics before what follows: wait for
+// every outstanding memory operation to be acknowledged.  (Device-scope
+// atomics are coherent across the chip's L2 slices; what the arrival counter
+// needs is only that a partition's additions are performed before its
+// arrival is counted.  A device-scope release fence would also write back
+// the whole L2, which costs far more than the kernel.)
+__device__ __forceinline__ void wait_memory_idle() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int FMT, bool SWAP, int MT, int NR, int PF>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     typedef typename AccT<FMT>::type acc_t;
     typedef typename AccT<FMT>::scalar acc_s;
@@ -321,6 +361,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     const int M = g.M, N = g.N, K = g.K;
     const int r16 = lane & 15, quarter = lane >> 4;
     const int G = (K + kGroup - 1) / kGroup;
+    const int R = min(16 * MT, M - m0);   // token rows that exist in this tile
 
     int nsub[NR];
     const uint8_t *wrow[NR];
@@ -337,92 +378,132 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[r][mt] = acc_t{0, 0, 0, 0};
 
-    float *s_scale = reinterpret_cast<float *>(smem + (size_t)MT * g.phase_blocks * 2048);
+    // Per-channel formats: the epilogue's token and channel scales are
+    // requested now, so their latency hides behind the weight stream.
+    // Swap-AB lanes need one token scale and 4 channel scales per sub-tile,
+    // Standard lanes 4 token scales and one channel scale.
+    float pre_sa[MT][SWAP ? 1 : 4], pre_sw[NR][SWAP ? 4 : 1];
+    if constexpr (FMT != FMT_BLOCK) {
+        if (g.nsplit == 1) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < (SWAP ? 1 : 4); ++i) {
+                    const int m = SWAP ? m0 + mt * 16 + r16 : m0 + mt * 16 + 4 * quarter + i;
+                    pre_sa[mt][i] = g.xs[min(m, M - 1)];
+                }
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int i = 0; i < (SWAP ? 4 : 1); ++i) {
+                    const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
+                    pre_sw[r][i] = g.wsc[min(n, N - 1)];
+                }
+        }
+    }
+
+    // issue the loads of absolute K block kb into a register slot (the block
+    // format also fetches each sub-tile's 128x128 weight-block scale)
+    auto issue = [&](v8i(&slot)[NR], float(&sws)[NR], int kb) {
+        const int k = kb * kGroup;
+        const bool full = k + kGroup <= K;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            slot[r] = load_w(wrow[r] + k, k + quarter * 32, K, full);
+            if constexpr (FMT == FMT_BLOCK)
+                sws[r] = g.wsc[(int64_t)(min(nsub[r], N - 1) / kGroup) * G + kb];
+        }
+    };
+
+    v8i wbuf[PF][NR];
+    float wsbuf[PF][NR];
+    const int kstep = g.kw;
 
     for (int pb0 = kb_begin; pb0 < kb_end; pb0 += g.phase_blocks) {
         const int nblk = min(kb_end - pb0, g.phase_blocks);
+        // weight requests for the first PF blocks of this phase go out first
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int b = kw + p * kstep;
+            if (b < nblk) issue(wbuf[p], wsbuf[p], pb0 + b);
+        }
         if (pb0 != kb_begin) __syncthreads();
-        // stage activation codes of this phase in fragment order
-        const int items = MT * 16 * nblk * 8;
+        // stage the activation codes of this phase: [block][half][quarter][row][16B]
+        const int items = R * nblk * 8;
         for (int it = threadIdx.x; it < items; it += nthreads) {
             const int c = it & 7;
             const int rest = it >> 3;
             const int b = rest % nblk;
             const int row = rest / nblk;
-            const int m = m0 + row;
             const int k = (pb0 + b) * kGroup + c * 16;
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (m < M && k < K) v = *reinterpret_cast<const uint4 *>(g.xq + (int64_t)m * K + k);
-            const int mt = row >> 4;
-            const int ln = (row & 15) + 16 * (c >> 1);
-            *reinterpret_cast<uint4 *>(smem + (((mt * nblk + b) * 2 + (c & 1)) * 64 + ln) * 16) = v;
+            if (k < K) v = *reinterpret_cast<const uint4 *>(g.xq + (int64_t)(m0 + row) * K + k);
+            *reinterpret_cast<uint4 *>(smem + (((b * 2 + (c & 1)) * 4 + (c >> 1)) * R + row) * 16) = v;
         }
+        float *s_scale = reinterpret_cast<float *>(smem + (size_t)g.phase_blocks * kGroup * R);
         if constexpr (FMT == FMT_BLOCK) {
-            for (int it = threadIdx.x; it < nblk * 16 * MT; it += nthreads) {
-                const int row = it % (16 * MT), b = it / (16 * MT);
-                const int m = m0 + row;
-                s_scale[b * 16 * MT + row] = m < M ? g.xs[(int64_t)m * G + pb0 + b] : 0.0f;
+            for (int it = threadIdx.x; it < nblk * R; it += nthreads) {
+                const int row = it % R, b = it / R;
+                s_scale[b * R + row] = g.xs[(int64_t)(m0 + row) * G + pb0 + b];
             }
         }
         __syncthreads();
 
-        // stream weight blocks: the wave's blocks are b = kw, kw + kw_n, ...
-        const int step = g.kw;
-        int b = kw;
-        v8i wcur[NR];
-        if (b < nblk) {
-            const int k = (pb0 + b) * kGroup;
-            const bool full = k + kGroup <= K;
+        bool more = kw < nblk;
+        for (int j = 0; more; j += PF) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) wcur[r] = load_w(wrow[r] + k, k + quarter * 32, K, full);
-        }
-        for (; b < nblk; b += step) {
-            const int bn = b + step;
-            v8i wnext[NR];
-            if (bn < nblk) {
-                const int k = (pb0 + bn) * kGroup;
-                const bool full = k + kGroup <= K;
+            for (int p = 0; p < PF; ++p) {
+                const int b = kw + (j + p) * kstep;
+                if (b >= nblk) {
+                    more = false;
+                    break;
+                }
+                // activation fragments of this block (zeros past row R)
+                v8i xf[MT];
 #pragma unroll
-                for (int r = 0; r < NR; ++r) wnext[r] = load_w(wrow[r] + k, k + quarter * 32, K, full);
-            }
-            v8i xf[MT];
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row = mt * 16 + r16;
+                    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+                    if (row < R) {
+                        const uint8_t *base = smem + (((b * 2) * 4 + quarter) * R + row) * 16;
+                        lo = *reinterpret_cast<const uint4 *>(base);
+                        hi = *reinterpret_cast<const uint4 *>(base + 4 * R * 16);
+                    }
+                    xf[mt] = join(lo, hi);
+                }
+                if constexpr (FMT == FMT_BLOCK) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t *base = smem + (size_t)((mt * nblk + b) * 2) * 1024 + lane * 16;
-                xf[mt] = join(*reinterpret_cast<const uint4 *>(base),
-                              *reinterpret_cast<const uint4 *>(base + 1024));
-            }
-            if constexpr (FMT == FMT_BLOCK) {
-                const int gk = pb0 + b;
+                    for (int r = 0; r < NR; ++r) {
+                        const float swv = wsbuf[p][r];
 #pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    const float swv = g.wsc[(int64_t)(min(nsub[r], N - 1) / kGroup) * G + gk];
+                        for (int mt = 0; mt < MT; ++mt) {
+                            const v4f t = SWAP ? block_mma<FMT>(wbuf[p][r], xf[mt], v4f{0, 0, 0, 0})
+                                               : block_mma<FMT>(xf[mt], wbuf[p][r], v4f{0, 0, 0, 0});
+                            const float *sc = s_scale + b * R;
+                            if (SWAP) {
+                                const int row = mt * 16 + r16;
+                                const float c = (row < R ? sc[row] : 0.0f) * swv;
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const v4f t = SWAP ? block_mma<FMT>(wcur[r], xf[mt], v4f{0, 0, 0, 0})
-                                           : block_mma<FMT>(xf[mt], wcur[r], v4f{0, 0, 0, 0});
-                        const float *sc = s_scale + b * 16 * MT + mt * 16;
-                        if (SWAP) {
-                            const float c = sc[r16] * swv;
+                                for (int i = 0; i < 4; ++i) acc[r][mt][i] += t[i] * c;
+                            } else {
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) acc[r][mt][i] += t[i] * c;
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) acc[r][mt][i] += t[i] * (sc[4 * quarter + i] * swv);
+                                for (int i = 0; i < 4; ++i) {
+                                    const int row = mt * 16 + 4 * quarter + i;
+                                    acc[r][mt][i] += t[i] * ((row < R ? sc[row] : 0.0f) * swv);
+                                }
+                            }
                         }
                     }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            acc[r][mt] = SWAP ? block_mma<FMT>(wbuf[p][r], xf[mt], acc[r][mt])
+                                              : block_mma<FMT>(xf[mt], wbuf[p][r], acc[r][mt]);
                 }
-            } else {
-#pragma unroll
-                for (int r = 0; r < NR; ++r)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        acc[r][mt] = SWAP ? block_mma<FMT>(wcur[r], xf[mt], acc[r][mt])
-                                          : block_mma<FMT>(xf[mt], wcur[r], acc[r][mt]);
-            }
-            if (bn < nblk) {
-#pragma unroll
-                for (int r = 0; r < NR; ++r) wcur[r] = wnext[r];
+                const int bn = b + PF * kstep;
+                if (bn < nblk) issue(wbuf[p], wsbuf[p], pb0 + bn);
             }
         }
     }
@@ -473,7 +554,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                     } else {
                         float o[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) o[i] = finish(acc[r][mt][i], m, n + i);
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (FMT == FMT_BLOCK) o[i] = acc[r][mt][i];
+                            else o[i] = ((float)acc[r][mt][i] * pre_sa[mt][0]) * pre_sw[r][i];
+                        }
                         if (g.out_type == QLIN_OUT_F32_ACC) {
                             *reinterpret_cast<float4 *>(static_cast<float *>(g.y) + (int64_t)m * N + n) =
                                 make_float4(o[0], o[1], o[2], o[3]);
@@ -490,12 +574,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                         const int m = m0 + mt * 16 + 4 * quarter + i;
                         if (m >= M) continue;
                         const int64_t idx = (int64_t)m * N + n;
+                        float o;
+                        if constexpr (FMT == FMT_BLOCK) o = acc[r][mt][i];
+                        else o = ((float)acc[r][mt][i] * pre_sa[mt][i]) * pre_sw[r][0];
                         if (g.out_type == QLIN_OUT_I32_ACC)
                             static_cast<int *>(g.y)[idx] = (int)acc[r][mt][i];
                         else if (g.out_type == QLIN_OUT_F32_ACC)
-                            static_cast<float *>(g.y)[idx] = finish(acc[r][mt][i], m, n);
+                            static_cast<float *>(g.y)[idx] = o;
                         else
-                            static_cast<uint16_t *>(g.y)[idx] = (uint16_t)bf16_bits(finish(acc[r][mt][i], m, n));
+                            static_cast<uint16_t *>(g.y)[idx] = (uint16_t)bf16_bits(o);
                     }
                 }
             }
@@ -503,8 +590,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         return;
     }
 
-    // Split-K: add this partition's sums into the workspace, then the last
-    // partition to arrive for this tile writes the output and re-zeroes it.
+    // Split-K (the partials of each partition are added into a zeroed
+    // workspace): atomically add this partition's sums, count the arrival;
+    // the last partition to arrive for this tile writes the output from the
+    // totals and re-zeroes the workspace and the counter.
     acc_s *ws = static_cast<acc_s *>(g.acc_ws);
     if (kw == 0) {
 #pragma unroll
@@ -516,24 +605,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 for (int i = 0; i < 4; ++i) {
                     const int m = SWAP ? m0 + mt * 16 + r16 : m0 + mt * 16 + 4 * quarter + i;
                     const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
-                    if (m < M) atomicAdd(&ws[(int64_t)m * N + n], acc[r][mt][i]);
+                    if (m < M)
+                        __hip_atomic_fetch_add(&ws[(int64_t)m * N + n], acc[r][mt][i], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
                 }
         }
     }
-    __threadfence();
+    wait_memory_idle();
     __syncthreads();
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
     if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&g.counters[tile], 1u, __ATOMIC_ACQ_REL,
+        const uint32_t prev = __hip_atomic_fetch_add(&g.counters[tile], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == (uint32_t)(g.nsplit - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    const int tm = min(16 * MT, M - m0);
     const int tn = min(TN, N - n_tile0);
-    for (int e = threadIdx.x; e < tm * tn; e += nthreads) {
+    for (int e = threadIdx.x; e < R * tn; e += nthreads) {
         const int m = m0 + e / tn;
         const int n = n_tile0 + e % tn;
         const int64_t idx = (int64_t)m * N + n;
@@ -560,10 +649,24 @@ hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, v
         const int groups = M * (K / kGroup);
         hipLaunchKernelGGL(quant_group_kernel, dim3((groups + 15) / 16), dim3(256), 0, s, xb, ldx,
                            M, K, q, xs);
-    } else if (fmt == FMT_I8) {
-        hipLaunchKernelGGL(quant_token_kernel<FMT_I8>, dim3(M), dim3(256), 0, s, xb, ldx, K, q, xs);
     } else {
-        hipLaunchKernelGGL(quant_token_kernel<FMT_FP8>, dim3(M), dim3(256), 0, s, xb, ldx, K, q, xs);
+        const int nch = K / 8;
+        const int cpt = (nch + kQuantThreads - 1) / kQuantThreads;
+#define QLIN_QT(F, C) \
+    hipLaunchKernelGGL((quant_token_kernel<F, C>), dim3(M), dim3(kQuantThreads), 0, s, xb, ldx, K, q, xs)
+#define QLIN_QT_ALL(F)                  \
+    if (cpt <= 1) QLIN_QT(F, 1);        \
+    else if (cpt <= 2) QLIN_QT(F, 2);   \
+    else if (cpt <= 4) QLIN_QT(F, 4);   \
+    else if (cpt <= 8) QLIN_QT(F, 8);   \
+    else QLIN_QT(F, 0);
+        if (fmt == FMT_I8) {
+            QLIN_QT_ALL(FMT_I8)
+        } else {
+            QLIN_QT_ALL(FMT_FP8)
+        }
+#undef QLIN_QT_ALL
+#undef QLIN_QT
     }
     return hipGetLastError();
 }
@@ -587,7 +690,7 @@ typedef void (*gemm_fn)(GemmLaunch);
 template <int FMT, bool SWAP>
 static gemm_fn pick(int tile_m, int nr) {
 #define QLIN_PICK(MT_, NR_) \
-    if (tile_m == 16 * MT_ && nr == NR_) return gemm_kernel<FMT, SWAP, MT_, NR_>;
+    if (tile_m == 16 * MT_ && nr == NR_) return gemm_kernel<FMT, SWAP, MT_, NR_, (NR_ >= 4 ? 2 : 4 / NR_ * 2)>;
     QLIN_PICK(1, 1) QLIN_PICK(1, 2) QLIN_PICK(1, 4)
     QLIN_PICK(2, 1) QLIN_PICK(2, 2) QLIN_PICK(2, 4)
 #undef QLIN_PICK

@@ -1,0 +1,201 @@
+"""Offline per-shape tuner: measures candidate schedules on the GPU and writes
+the selection table that qlin_select_variant reads.
+
+"Building a High-Performance and Portable vLLM Linear Backend with Helion",
+sections "Per-shape Config Tuning" (each (shape, num_tokens) in the tuned
+range gets its own configuration) and "Enable CUDA Graph for Autotuner
+Benchmarking" (candidates are timed the way they run in production, under
+graph replay).  Here the search is exhaustive over a fixed candidate grid
+(schedule, tile, split factor, wave layout); each candidate is timed as a
+hipGraph of back-to-back launches over distinct weight copies (>= 1 GiB in
+total, so the Infinity Cache cannot hold them), coarse pass first, then the
+best few again with more replays.
+
+Usage:
+  python -m skinny_bit_gemm_amd.tune --shape fp8_dynamic,4096,2048 ... \\
+      [--m 1,2,4,8,16,24,32] [--out tables/gfx950.tbl] [--report file.json]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import skinny_bit_gemm_amd as q
+
+FMT_NAMES = {q.QLIN_FP8_DYNAMIC: "fp8_dynamic", q.QLIN_W8A8_INT8: "w8a8_int8",
+             q.QLIN_BLOCK_FP8: "block_fp8"}
+FMT_IDS = {v: k for k, v in FMT_NAMES.items()}
+
+# (tile_n, waves, k_waves)
+TILES = [(16, 1, 1), (16, 2, 2), (16, 4, 4), (16, 8, 8), (32, 1, 1), (32, 2, 2), (32, 4, 4),
+         (32, 4, 2), (32, 8, 8), (32, 8, 4), (64, 1, 1), (64, 2, 1), (64, 4, 4), (64, 4, 2),
+         (64, 4, 1), (64, 8, 4), (64, 8, 2), (128, 4, 1), (128, 8, 2), (128, 8, 1)]
+SPLITS = [1, 2, 3, 4, 6, 8, 12, 16, 24, 32]
+
+
+def candidates(fmt, M, N, K):
+    nkb = -(-K // 128)
+    seen = set()
+    out = []
+    tile_m = 16 if M <= 16 else 32
+    for swap in (0, 1):
+        for (tn, waves, kw) in TILES:
+            for split in SPLITS:
+                kbs = -(-nkb // split)
+                eff = -(-nkb // kbs)
+                key = (swap, tn, waves, kw, kbs)
+                if key in seen or kbs < kw:
+                    continue
+                c = q.make_config(swap, eff, tile_m, tn, waves, kw)
+                if q.qlin_validate_config(fmt, M, N, K, c) != 0:
+                    continue
+                wgs = -(-N // tn) * -(-M // tile_m) * eff
+                if wgs < 16 or wgs > 16384:
+                    continue
+                seen.add(key)
+                out.append(c)
+    return out
+
+
+class Bench:
+    """Device buffers for timing one (fmt, M, N, K) point."""
+
+    def __init__(self, fmt, M, N, K, min_bytes=1 << 30):
+        import torch
+        self.torch = torch
+        self.fmt, self.M, self.N, self.K = fmt, M, N, K
+        dev = "cuda"
+        self.R = max(2, -(-min_bytes // (N * K)))
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+
+        def codes(shape):
+            t = torch.randint(-120, 120, shape, dtype=torch.int8, device=dev, generator=g)
+            if fmt != q.QLIN_W8A8_INT8:            # finite, modest fp8 codes
+                t = (t.view(torch.uint8) & 0xB7)
+            return t
+        self.W = [codes((N, K)) for _ in range(self.R)]
+        self.ws = torch.rand(q.scales_shape(fmt, N, K, True), device=dev, generator=g) * 1e-2
+        self.xq = codes((M, K))
+        self.xs = torch.rand(q.scales_shape(fmt, M, K, False), device=dev, generator=g)
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.stream = torch.cuda.Stream()
+
+    def time(self, cfg, replays=3):
+        torch = self.torch
+        nb = q.qlin_workspace_bytes(self.fmt, self.M, self.N, self.K, cfg)
+        work = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+        st = self.stream
+        with torch.cuda.stream(st):
+            q.qlin_gemm(self.fmt, self.M, self.N, self.K, self.xq, self.xs, self.W[0], self.ws,
+                        self.y, q.QLIN_OUT_BF16, cfg, work, stream=st)
+            q.qlin_graph_begin(st)
+            try:
+                for w in self.W:
+                    q.qlin_gemm(self.fmt, self.M, self.N, self.K, self.xq, self.xs, w, self.ws,
+                                self.y, q.QLIN_OUT_BF16, cfg, work, stream=st)
+            finally:
+                gr = q.qlin_graph_end(st)
+            q.qlin_graph_launch(gr, st)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(replays):
+                q.qlin_graph_launch(gr, st)
+            e1.record(st)
+            torch.cuda.synchronize()
+            q.qlin_graph_destroy(gr)
+        return e0.elapsed_time(e1) * 1e3 / (replays * self.R)
+
+    def free(self):
+        self.W = None
+        self.torch.cuda.empty_cache()
+
+
+def variant_class(c):
+    if c.split_k > 1:
+        return "splitk"
+    return "swap_ab" if c.swap_ab else "standard"
+
+
+def tune_point(fmt, M, N, K, keep=6):
+    b = Bench(fmt, M, N, K)
+    cands = candidates(fmt, M, N, K)
+    coarse = []
+    for c in cands:
+        coarse.append((b.time(c, replays=1), c))
+    coarse.sort(key=lambda t: t[0])
+    fine = []
+    for _, c in coarse[:keep]:
+        fine.append((b.time(c, replays=5), c))
+    fine.sort(key=lambda t: t[0])
+    best_by_class = {}
+    for t, c in coarse:
+        cls = variant_class(c)
+        if cls not in best_by_class:
+            best_by_class[cls] = (t, c)
+    b.free()
+    return fine[0], best_by_class, len(cands)
+
+
+def algorithmic_bytes(fmt, M, N, K):
+    if fmt == q.QLIN_BLOCK_FP8:
+        wsc, asc = 4 * (N // 128) * (K // 128), 4 * M * (K // 128)
+    else:
+        wsc, asc = 4 * N, 4 * M
+    return N * K + wsc + M * K + asc + 2 * M * N
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--shape", action="append", default=[], help="fmt,N,K")
+    ap.add_argument("--m", default="1,2,4,8,16,24,32")
+    ap.add_argument("--out", default=os.path.join(os.path.dirname(__file__), "tables", "gfx950.tbl"))
+    ap.add_argument("--merge", action="store_true", help="keep existing entries of --out")
+    ap.add_argument("--report", default=None)
+    args = ap.parse_args(argv)
+    Ms = [int(v) for v in args.m.split(",")]
+    q.lib()
+    entries = {}
+    if args.merge and os.path.exists(args.out):
+        with open(args.out) as f:
+            for line in f:
+                p = line.split("#")[0].split()
+                if len(p) == 10:
+                    entries[(p[0], int(p[1]), int(p[2]), int(p[3]))] = p[4:]
+    report = []
+    t_start = time.time()
+    for spec in args.shape:
+        fname, N, K = spec.split(",")
+        fmt, N, K = FMT_IDS[fname], int(N), int(K)
+        for M in Ms:
+            (t, c), by_class, n = tune_point(fmt, M, N, K)
+            gbs = algorithmic_bytes(fmt, M, N, K) / t / 1e3
+            entries[(fname, N, K, M)] = [str(v) for v in (c.swap_ab, c.split_k, c.tile_m, c.tile_n,
+                                                         c.waves, c.k_waves)]
+            rec = {"fmt": fname, "N": N, "K": K, "M": M, "us": round(t, 3), "GBps": round(gbs, 1),
+                   "cfg": c.as_dict(), "candidates": n,
+                   "best_by_class": {k: {"us": round(v[0], 3), "cfg": v[1].as_dict()}
+                                     for k, v in by_class.items()}}
+            report.append(rec)
+            print(f"[tune {time.time() - t_start:6.1f}s] {fname} N={N} K={K} M={M}: {t:.2f} us "
+                  f"{gbs:.0f} GB/s {c}  (" + ", ".join(f"{k} {v[0]:.2f}" for k, v in by_class.items())
+                  + ")", flush=True)
+    os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
+    with open(args.out, "w") as f:
+        f.write(f"qlin-table {q.qlin_abi_version()} gfx950\n")
+        f.write("# measured on MI355X by skinny_bit_gemm_amd.tune (hipGraph replay, rotating weights)\n")
+        f.write("# format N K M swap_ab split_k tile_m tile_n waves k_waves\n")
+        for k in sorted(entries):
+            f.write(" ".join([k[0], str(k[1]), str(k[2]), str(k[3])] + entries[k]) + "\n")
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(report, f, indent=1)
+    print(f"wrote {len(entries)} entries to {args.out}", flush=True)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+"""The C ABI on the host (no GPU): the library loads, exports every symbol
+include/qlin.h declares, rejects bad arguments before any HIP call, and
+reads / rejects selection tables.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import skinny_bit_gemm_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlin.h")
+
+FP8, I8, BLK = q.QLIN_FP8_DYNAMIC, q.QLIN_W8A8_INT8, q.QLIN_BLOCK_FP8
+OK, EINVAL, EALIGN, ESHAPE, EWS, ENOCFG, ETABLE = 0, 1, 2, 3, 4, 5, 6
+A = 1 << 20     # a fake, 16-byte aligned "device address" (never dereferenced)
+
+
+@pytest.fixture(autouse=True)
+def _restore_table():
+    yield
+    q.qlin_set_strict(False)
+    if os.path.exists(q.TABLE_PATH):
+        q.qlin_load_table(q.TABLE_PATH)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(qlin_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = q.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in qlin.h but not exported"
+    assert set(names) == set(q.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    assert q.qlin_abi_version() == 1
+    for st in range(8):
+        assert q.qlin_status_str(st)
+    assert "strict" in q.qlin_status_str(ENOCFG)
+
+
+def gemm(fmt=FP8, M=4, N=256, K=512, xq=A, xs=A, wq=A, ws=A, y=A, out=0, cfg=None, work=None, wsb=0):
+    return q.qlin_gemm(fmt, M, N, K, xq, xs, wq, ws, y, out, cfg, work, wsb, stream=0,
+                       raise_on_error=False)
+
+
+def test_gemm_rejects_bad_arguments():
+    assert gemm(fmt=7) == EINVAL
+    assert gemm(out=5) == EINVAL
+    assert gemm(fmt=FP8, out=q.QLIN_OUT_I32_ACC) == EINVAL      # int32 sums: int8 only
+    assert gemm(xq=None) == EINVAL
+    assert gemm(y=None) == EINVAL
+    assert gemm(wq=A + 8) == EALIGN
+    assert gemm(xs=A + 2) == EALIGN
+    assert gemm(N=100) == ESHAPE                   # N % 16
+    assert gemm(K=520) == ESHAPE                   # K % 16
+    assert gemm(M=-1) == ESHAPE
+    assert gemm(fmt=BLK, K=640 + 16) == ESHAPE     # block format: K % 128
+    assert gemm(fmt=BLK, N=256 + 16) == ESHAPE     # block format: N % 128
+    assert gemm(fmt=I8, K=133_120 + 128) == ESHAPE  # int32 sums could overflow
+
+
+def test_gemm_rejects_bad_configs():
+    bad = [q.make_config(swap_ab=2), q.make_config(split_k=0), q.make_config(split_k=65),
+           q.make_config(tile_m=8), q.make_config(waves=3, k_waves=1),
+           q.make_config(waves=4, k_waves=3), q.make_config(tile_n=24, waves=1, k_waves=1),
+           q.make_config(tile_n=512, waves=1, k_waves=1),
+           q.make_config(tile_n=32, waves=4, k_waves=1)]   # 4 column waves need tile_n >= 64
+    for c in bad:
+        assert gemm(cfg=c) == EINVAL, c
+        assert q.qlin_validate_config(FP8, 4, 256, 512, c) == EINVAL
+
+
+def test_split_k_workspace_is_checked_before_launch():
+    c = q.make_config(swap_ab=1, split_k=4, tile_m=16, tile_n=32, waves=4, k_waves=4)
+    need = q.qlin_workspace_bytes(FP8, 4, 256, 2048, c)
+    assert need >= 4 * 256 * 4
+    assert gemm(K=2048, cfg=c, work=None, wsb=0) == EWS
+    assert gemm(K=2048, cfg=c, work=A, wsb=need - 1) == EWS
+    assert gemm(K=2048, cfg=c, work=A + 4, wsb=need) == EALIGN
+    # one partition only (K fits one split): no workspace needed
+    c1 = q.make_config(swap_ab=1, split_k=4, tile_m=16, tile_n=32, waves=4, k_waves=4)
+    assert q.qlin_workspace_bytes(FP8, 4, 256, 128, c1) == 0
+
+
+def test_quantize_rejects_bad_arguments():
+    f = lambda *a, **k: q.qlin_quantize_act(*a, stream=0, raise_on_error=False, **k)
+    assert f(9, 4, 512, A, 512, A, A) == EINVAL
+    assert f(FP8, 4, 520, A, 520, A, A) == ESHAPE
+    assert f(BLK, 4, 528, A, 528, A, A) == ESHAPE
+    assert f(FP8, 4, 512, A, 500, A, A) == EALIGN       # ldx < K
+    assert f(FP8, 4, 512, A, 516, A, A) == EALIGN       # ldx % 8
+    assert f(FP8, 4, 512, A + 2, 512, A, A) == EALIGN
+    assert f(FP8, 4, 512, None, 512, A, A) == EINVAL
+    assert f(FP8, 0, 512, A, 512, A, A) == OK           # nothing to do, nothing launched
+    g = lambda *a: q.qlin_quantize_weight(*a, stream=0, raise_on_error=False)
+    assert g(FP8, 100, 512, A, A, A) == ESHAPE
+    assert g(BLK, 256, 384 + 16, A, A, A) == ESHAPE
+    assert g(I8, 256, 512, A, None, A) == EINVAL
+
+
+def test_zero_tokens_gemm_is_ok_without_launch():
+    assert gemm(M=0) == OK
+
+
+def test_token_bucket_rounding_and_default_rule():
+    # no entry for this odd shape: permissive mode answers with the built-in rule
+    c = q.qlin_select_variant(FP8, 3, 1024, 1024)
+    assert c.tile_m == 16 and c.swap_ab == 1
+    c32 = q.qlin_select_variant(FP8, 32, 1024, 1024)
+    assert c32.tile_m == 32 and c32.swap_ab == 0
+    for M in (1, 5, 31, 100, 600):
+        c = q.qlin_select_variant(I8, M, 2048, 4096)
+        assert q.qlin_validate_config(I8, M, 2048, 4096, c) == OK
+
+
+def write_table(tmp_path, body, header="qlin-table 1 gfx950"):
+    p = tmp_path / "t.tbl"
+    p.write_text(header + "\n" + body)
+    return str(p)
+
+
+def test_table_load_lookup_and_bucket_round_up(tmp_path):
+    path = write_table(tmp_path, "# comment\n"
+                       "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n"
+                       "fp8_dynamic 1024 1024 32 0 4 32 32 4 4   # trailing comment\n")
+    assert q.qlin_load_table(path) == OK
+    assert q.qlin_table_entries() == 2
+    c = q.qlin_select_variant(FP8, 3, 1024, 1024)           # 3 -> bucket 4
+    assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves) == (1, 2, 16, 64, 4, 2)
+    c = q.qlin_select_variant(FP8, 25, 1024, 1024)          # 25 -> bucket 32
+    assert (c.swap_ab, c.split_k, c.tile_m) == (0, 4, 32)
+
+
+def test_strict_mode_missing_entry_is_an_error(tmp_path):
+    path = write_table(tmp_path, "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n")
+    assert q.qlin_load_table(path) == OK
+    q.qlin_set_strict(True)
+    with pytest.raises(q.QlinError) as e:
+        q.qlin_select_variant(FP8, 8, 1024, 1024)
+    assert e.value.status == ENOCFG
+    assert gemm(N=1024, K=1024, M=8) == ENOCFG
+    # a present entry and a forced config still work
+    assert q.qlin_select_variant(FP8, 4, 1024, 1024).split_k == 2
+    q.qlin_set_strict(False)
+    assert q.qlin_select_variant(FP8, 8, 1024, 1024).tile_m == 16
+
+
+@pytest.mark.parametrize("header,body", [
+    ("qlin-table 1 gfx942", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n"),     # wrong arch
+    ("qlin-table 2 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n"),     # wrong version
+    ("qlin-table 1 gfx950", "fp4 1024 1024 4 1 2 16 64 4 2\n"),             # unknown format
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 64 4\n"),       # short line
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 5 1 2 16 64 4 2\n"),     # 5 is no bucket
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 48 4 2\n"),     # invalid tile
+    ("nonsense", ""),
+])
+def test_corrupt_tables_are_rejected(tmp_path, header, body):
+    good = write_table(tmp_path, "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n")
+    assert q.qlin_load_table(good) == OK
+    p = tmp_path / "bad.tbl"
+    p.write_text(header + "\n" + body)
+    assert q.qlin_load_table(str(p), raise_on_error=False) == ETABLE
+    # the previously loaded table stays in force
+    assert q.qlin_table_entries() == 1
+    assert q.qlin_load_table(str(tmp_path / "missing.tbl"), raise_on_error=False) == ETABLE
+
+
+def test_installed_table_is_valid():
+    if not os.path.exists(q.TABLE_PATH):
+        pytest.skip("no installed table")
+    assert q.qlin_load_table(q.TABLE_PATH) == OK
+    assert q.qlin_table_entries() > 0
+
+
+def test_graph_calls_reject_null_handles():
+    L = q.lib()
+    assert L.qlin_graph_launch(None, None) == EINVAL
+    assert L.qlin_graph_destroy(None) == EINVAL
+    assert L.qlin_graph_begin(None) == EINVAL
+    h = ctypes.c_void_p()
+    assert L.qlin_graph_end(None, ctypes.byref(h)) == EINVAL
+
+
+def test_one_hip_runtime_is_mapped():
+    """The library binds to torch's HIP runtime instead of mapping a second
+    copy (a second runtime would not know torch's stream handles)."""
+    import subprocess
+    import sys
+    code = ("import skinny_bit_gemm_amd as q; q.lib();"
+            "m = open('/proc/self/maps').read();"
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         check=True).stdout.strip().splitlines()[-1]
+    assert out == "1"
