@@ -2,8 +2,9 @@
 
 A step is one pass of the hot path over one batch of synthetic inputs: for
 every token count M of the workload and every linear layer of the model, the
-activation quantizer and the GEMM, replayed from a hipGraph captured once
-(the decode path runs only under graph replay).  Weights live in HBM as
+whole quantized linear (qlin_linear: activation quantization and GEMM, as one
+fused kernel or two, per the selection table), replayed from a hipGraph
+captured once (the decode path runs only under graph replay).  Weights live in HBM as
 R distinct rotating copies (>= 1 GiB in total) so the 256 MiB Infinity Cache
 cannot serve them; activations, scales and outputs are resident too.
 
@@ -66,9 +67,11 @@ class Linear:
         self.qbytes = wl.quant_bytes(fmt, M, layer.K)
         self.flops = wl.flops(M, layer.N, layer.K)
 
-    def quant(self, stream):
+    def layer(self, stream):
+        """The whole decode linear: quantize + GEMM (one or two kernels, as tuned)."""
         import skinny_bit_gemm_amd as q
-        q.qlin_quantize_act(self.fmt, self.M, self.K, self.x, self.K, self.xq, self.xs, stream)
+        q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, self.wq,
+                      self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work, stream=stream)
 
     def gemm(self, stream, wq=None):
         import skinny_bit_gemm_amd as q
@@ -172,11 +175,10 @@ def main():
     with torch.cuda.stream(stream):
         # eager once (also checks every launch is accepted), then capture
         for lin in sets[0]:
-            lin.quant(stream)
+            lin.layer(stream)
             lin.gemm(stream)
         torch.cuda.synchronize()
-        step_graphs = [capture(stream, lambda ls=ls: [(l.quant(stream), l.gemm(stream)) for l in ls])
-                       for ls in sets]
+        step_graphs = [capture(stream, lambda ls=ls: [l.layer(stream) for l in ls]) for ls in sets]
         gemm_graphs = [capture(stream, lambda ls=ls: [l.gemm(stream) for l in ls]) for ls in sets]
         torch.cuda.synchronize()
 

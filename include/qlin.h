@@ -76,18 +76,28 @@ typedef enum {
 } qlin_status;
 
 /* One schedule of the contraction (section "Kernel Implementation": the
- * split_k and swap_ab tunables, plus the tile shape).
- *   swap_ab  0: tokens fill the matrix-core row operand (Standard);
- *            1: weight rows fill it and the result is transposed back,
- *               y = (W_q . x_q^T)^T (Swap-AB).
- *   split_k  number of K partitions handled by separate workgroups, 1..64;
- *            each covers ceil(K / split_k) rounded up to 128 (the effective
- *            count can be lower); partial sums are added in a workspace.
- *   tile_m   tokens per tile: 16 or 32.
- *   tile_n   output channels per workgroup: a multiple of 16, <= 256.
- *   waves    64-lane waves per workgroup: 1, 2, 4 or 8.
- *   k_waves  how many of those waves split the workgroup's K range
- *            (the rest split tile_n); divides waves.                        */
+ * split_k and swap_ab tunables, plus the tile shape and how the pieces are
+ * put back together).
+ *   swap_ab    0: tokens fill the matrix-core row operand (Standard);
+ *              1: weight rows fill it and the result is transposed back,
+ *                 y = (W_q . x_q^T)^T (Swap-AB).
+ *   split_k    number of K partitions handled by separate workgroups, 1..64;
+ *              each covers ceil(K / split_k) rounded up to 128 (the effective
+ *              count can be lower).
+ *   tile_m     tokens per tile: 16 or 32.
+ *   tile_n     output channels per workgroup: a multiple of 16, <= 256.
+ *   waves      64-lane waves per workgroup: 1, 2, 4 or 8.
+ *   k_waves    how many of those waves split the workgroup's K range
+ *              (the rest split tile_n); divides waves.
+ *   reduce     how Split-K partitions are combined: 0 = every partition
+ *              stores its partial sums in its own workspace slice and the
+ *              last to arrive adds them in partition order (any format);
+ *              1 = exact packed 64-bit integer atomics (W8A8_INT8, and
+ *              FP8_DYNAMIC with K <= 40960).  Both give results that do
+ *              not depend on the order partitions finish in.
+ *   fuse_quant qlin_linear only: 1 = each GEMM workgroup quantizes the
+ *              activations it needs itself (one kernel instead of two;
+ *              needs tile_m 16); ignored by qlin_gemm.                      */
 typedef struct {
     int32_t swap_ab;
     int32_t split_k;
@@ -95,6 +105,8 @@ typedef struct {
     int32_t tile_n;
     int32_t waves;
     int32_t k_waves;
+    int32_t reduce;
+    int32_t fuse_quant;
 } qlin_config;
 
 /* Activation quantization (per token, or per token and 1x128 group for
@@ -122,14 +134,25 @@ qlin_status qlin_quantize_weight(qlin_format fmt, int N, int K, const float *w, 
  *                 otherwise that schedule is forced (it must be valid)
  *   workspace     needed when the schedule splits K: at least
  *                 qlin_workspace_bytes(...) bytes, zero-filled before its
- *                 first use; every call leaves it zero again.  Calls that
- *                 overlap in time must not share a workspace.
+ *                 first use; every call leaves it zero again, so one buffer
+ *                 can serve calls of any shape and schedule that fit it.
+ *                 Calls that overlap in time must not share a workspace.
  * Returns QLIN_ERR_NO_CONFIG in strict mode when cfg is NULL and the table
  * has no entry for (fmt, N, K, bucket(M)). */
 qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq,
                       const float *x_scales, const void *wq, const float *w_scales, void *y,
                       qlin_out_type out_type, const qlin_config *cfg, void *workspace,
                       size_t ws_bytes, void *stream);
+
+/* The whole layer: quantize x (as qlin_quantize_act; xq and x_scales are
+ * written) and compute y (as qlin_gemm).  With cfg->fuse_quant (or the
+ * table's choice when cfg is NULL) this is one kernel launch, else two.
+ * Arguments, layouts and errors are those of the two calls; x must not
+ * alias xq, x_scales or y. */
+qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
+                        float *x_scales, const void *wq, const float *w_scales, void *y,
+                        qlin_out_type out_type, const qlin_config *cfg, void *workspace,
+                        size_t ws_bytes, void *stream);
 
 /* Schedule lookup (host only, no device work).  M rounds up to the next
  * tuned token bucket {1,2,4,8,16,24,32} (section "Per-shape Config Tuning"),

@@ -25,7 +25,7 @@ STATUS = {
 
 # every symbol include/qlin.h declares
 EXPORTS = (
-    "qlin_quantize_act", "qlin_quantize_weight", "qlin_gemm", "qlin_select_variant",
+    "qlin_quantize_act", "qlin_quantize_weight", "qlin_gemm", "qlin_linear", "qlin_select_variant",
     "qlin_workspace_bytes", "qlin_validate_config", "qlin_load_table", "qlin_set_strict",
     "qlin_table_entries", "qlin_graph_begin", "qlin_graph_end", "qlin_graph_launch",
     "qlin_graph_destroy", "qlin_status_str", "qlin_abi_version", "qlin_last_hip_error",
@@ -45,7 +45,8 @@ class QlinError(RuntimeError):
 class qlin_config(ctypes.Structure):
     _fields_ = [("swap_ab", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("k_waves", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("k_waves", ctypes.c_int32),
+                ("reduce", ctypes.c_int32), ("fuse_quant", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: int(getattr(self, f)) for f, _ in self._fields_}
@@ -54,8 +55,9 @@ class qlin_config(ctypes.Structure):
         return "qlin_config(%s)" % ", ".join(f"{k}={v}" for k, v in self.as_dict().items())
 
 
-def make_config(swap_ab=0, split_k=1, tile_m=16, tile_n=32, waves=4, k_waves=4) -> qlin_config:
-    return qlin_config(swap_ab, split_k, tile_m, tile_n, waves, k_waves)
+def make_config(swap_ab=0, split_k=1, tile_m=16, tile_n=32, waves=4, k_waves=4, reduce=0,
+                fuse_quant=0) -> qlin_config:
+    return qlin_config(swap_ab, split_k, tile_m, tile_n, waves, k_waves, reduce, fuse_quant)
 
 
 _lib = None
@@ -82,6 +84,8 @@ def lib():
         L.qlin_quantize_weight.argtypes = [_I, _I, _I, _P, _P, _P, _P]
         L.qlin_gemm.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _I,
                                 ctypes.POINTER(qlin_config), _P, _SZ, _P]
+        L.qlin_linear.argtypes = [_I, _I, _I, _I, _P, _I64, _P, _P, _P, _P, _P, _I,
+                                  ctypes.POINTER(qlin_config), _P, _SZ, _P]
         L.qlin_select_variant.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config)]
         L.qlin_workspace_bytes.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config),
                                            ctypes.POINTER(_SZ)]
@@ -146,6 +150,18 @@ def qlin_gemm(fmt, M, N, K, xq, x_scales, wq, w_scales, y, out_type=QLIN_OUT_BF1
     st = lib().qlin_gemm(fmt, M, N, K, _ptr(xq), _ptr(x_scales), _ptr(wq), _ptr(w_scales), _ptr(y),
                          out_type, cptr, _ptr(workspace), ws_bytes, _stream(stream))
     return _check(st, "qlin_gemm", raise_on_error)
+
+
+def qlin_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type=QLIN_OUT_BF16,
+                cfg=None, workspace=None, ws_bytes=None, stream=None, raise_on_error=True):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None and \
+            not isinstance(workspace, int) else 0
+    cptr = ctypes.byref(cfg) if cfg is not None else None
+    st = lib().qlin_linear(fmt, M, N, K, _ptr(x), ldx, _ptr(xq), _ptr(x_scales), _ptr(wq),
+                           _ptr(w_scales), _ptr(y), out_type, cptr, _ptr(workspace), ws_bytes,
+                           _stream(stream))
+    return _check(st, "qlin_linear", raise_on_error)
 
 
 def qlin_select_variant(fmt, M, N, K) -> qlin_config:

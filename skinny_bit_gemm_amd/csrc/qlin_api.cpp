@@ -54,7 +54,8 @@ qlin_status resolve_config(qlin_format fmt, int M, int N, int K, const qlin_conf
 
 }  // namespace
 
-qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c, Plan *p) {
+qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c, bool fused,
+                      Plan *p) {
     if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
     if (M < 1) M = 1;
     if (c.swap_ab != 0 && c.swap_ab != 1) return QLIN_ERR_INVALID_ARG;
@@ -62,10 +63,19 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     if (c.tile_m != 16 && c.tile_m != 32) return QLIN_ERR_INVALID_ARG;
     if (c.waves != 1 && c.waves != 2 && c.waves != 4 && c.waves != 8) return QLIN_ERR_INVALID_ARG;
     if (c.k_waves < 1 || c.k_waves > c.waves || c.waves % c.k_waves != 0) return QLIN_ERR_INVALID_ARG;
+    if (c.reduce != 0 && c.reduce != 1) return QLIN_ERR_INVALID_ARG;
+    if (c.fuse_quant != 0 && c.fuse_quant != 1) return QLIN_ERR_INVALID_ARG;
+    // int8 sums (K <= 133120) and fp8 sums in units of 2^-18 stay below 2^51
+    // in magnitude while K <= 40960: only those partials can be added as
+    // packed 64-bit integers
+    if (c.reduce == 1 && !(fmt == QLIN_W8A8_INT8 || (fmt == QLIN_FP8_DYNAMIC && K <= 40960)))
+        return QLIN_ERR_INVALID_ARG;
+    const bool fuse = fused && c.fuse_quant == 1;
+    if (c.fuse_quant == 1 && c.tile_m != 16) return QLIN_ERR_INVALID_ARG;
     const int nw = c.waves / c.k_waves;
     if (c.tile_n < 16 || c.tile_n > 256 || c.tile_n % (16 * nw) != 0) return QLIN_ERR_INVALID_ARG;
     const int nr = c.tile_n / (16 * nw);
-    if (!gemm_variant_exists(fmt, c.tile_m, nr)) return QLIN_ERR_INVALID_ARG;
+    if (!gemm_variant_exists(fmt, c.tile_m, nr, fuse)) return QLIN_ERR_INVALID_ARG;
     const int mt = c.tile_m / 16;
     p->tile_m = c.tile_m;
     p->tile_n = c.tile_n;
@@ -73,6 +83,7 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     p->nw = nw;
     p->kw = c.k_waves;
     p->waves = c.waves;
+    p->fuse = fuse;
     p->nkb = (K + kGroup - 1) / kGroup;
     p->kb_per_split = (p->nkb + c.split_k - 1) / c.split_k;
     p->nsplit = (p->nkb + p->kb_per_split - 1) / p->kb_per_split;
@@ -89,11 +100,15 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     p->lds_bytes = lds;
     p->n_tiles = (N + c.tile_n - 1) / c.tile_n;
     p->m_tiles = (M + c.tile_m - 1) / c.tile_m;
+    // workspace: [arrival counters][packed int64 sums, or one slice of
+    // 32-bit partial sums per partition]; all of it is zero between calls
+    p->packed = p->nsplit > 1 && c.reduce == 1;
     if (p->nsplit > 1) {
-        p->ws_acc_bytes = align256((size_t)M * N * 4);
-        p->ws_bytes = p->ws_acc_bytes + align256((size_t)p->n_tiles * p->m_tiles * 4);
+        p->ws_counter_bytes = align256((size_t)p->n_tiles * p->m_tiles * 4);
+        const size_t sums = p->packed ? (size_t)M * N * 8 : (size_t)p->nsplit * M * N * 4;
+        p->ws_bytes = p->ws_counter_bytes + align256(sums);
     } else {
-        p->ws_acc_bytes = 0;
+        p->ws_counter_bytes = 0;
         p->ws_bytes = 0;
     }
     return QLIN_OK;
@@ -135,7 +150,7 @@ qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qli
     if (st != QLIN_OK) return st;
     if (!cfg) return QLIN_ERR_INVALID_ARG;
     Plan p;
-    return make_plan(fmt, M, N, K, *cfg, &p);
+    return make_plan(fmt, M, N, K, *cfg, true, &p);
 }
 
 qlin_status qlin_select_variant(qlin_format fmt, int M, int N, int K, qlin_config *out) {
@@ -155,46 +170,47 @@ qlin_status qlin_workspace_bytes(qlin_format fmt, int M, int N, int K, const qli
     st = resolve_config(fmt, M, N, K, cfg, &c);
     if (st != QLIN_OK) return st;
     Plan p;
-    st = make_plan(fmt, M, N, K, c, &p);
+    st = make_plan(fmt, M, N, K, c, true, &p);
     if (st != QLIN_OK) return st;
     *bytes = p.ws_bytes;
     return QLIN_OK;
 }
 
-qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, const float *x_scales,
-                      const void *wq, const float *w_scales, void *y, qlin_out_type out_type,
-                      const qlin_config *cfg, void *workspace, size_t ws_bytes, void *stream) {
+// Checks shared by qlin_gemm and qlin_linear (everything but the
+// activations); fills *c and *p.
+static qlin_status check_gemm(qlin_format fmt, int M, int N, int K, const float *x_scales,
+                              const void *wq, const float *w_scales, void *y,
+                              qlin_out_type out_type, const qlin_config *cfg, void *workspace,
+                              size_t ws_bytes, bool fused, qlin_config *c, Plan *p) {
     if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
     if (out_type != QLIN_OUT_BF16 && out_type != QLIN_OUT_F32_ACC && out_type != QLIN_OUT_I32_ACC)
         return QLIN_ERR_INVALID_ARG;
     if (out_type == QLIN_OUT_I32_ACC && fmt != QLIN_W8A8_INT8) return QLIN_ERR_INVALID_ARG;
     qlin_status st = shape_ok(fmt, M, N, K);
     if (st != QLIN_OK) return st;
-    if (!xq || !x_scales || !wq || !w_scales || !y) return QLIN_ERR_INVALID_ARG;
-    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(x_scales) ||
-        !aligned4(w_scales))
+    if (!x_scales || !wq || !w_scales || !y) return QLIN_ERR_INVALID_ARG;
+    if (!aligned16(wq) || !aligned16(y) || !aligned4(x_scales) || !aligned4(w_scales))
         return QLIN_ERR_ALIGNMENT;
-    qlin_config c;
-    st = resolve_config(fmt, M, N, K, cfg, &c);
+    st = resolve_config(fmt, M, N, K, cfg, c);
     if (st != QLIN_OK) return st;
-    Plan p;
-    st = make_plan(fmt, M, N, K, c, &p);
+    st = make_plan(fmt, M, N, K, *c, fused, p);
     if (st != QLIN_OK) return st;
-    if (p.ws_bytes > 0) {
-        if (!workspace || ws_bytes < p.ws_bytes) return QLIN_ERR_WORKSPACE;
+    if (p->ws_bytes > 0) {
+        if (!workspace || ws_bytes < p->ws_bytes) return QLIN_ERR_WORKSPACE;
         if (!aligned16(workspace)) return QLIN_ERR_ALIGNMENT;
     }
-    if (M == 0) return QLIN_OK;
+    return QLIN_OK;
+}
 
-    GemmLaunch g;
-    g.xq = static_cast<const uint8_t *>(xq);
-    g.xs = x_scales;
+static GemmLaunch launch_args(const Plan &p, int M, int N, int K, const void *wq,
+                              const float *w_scales, void *y, qlin_out_type out_type,
+                              void *workspace) {
+    GemmLaunch g = {};
     g.wq = static_cast<const uint8_t *>(wq);
     g.wsc = w_scales;
     g.y = y;
-    g.acc_ws = p.ws_bytes ? workspace : nullptr;
-    g.counters = p.ws_bytes ? reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + p.ws_acc_bytes)
-                            : nullptr;
+    g.counters = p.ws_bytes ? static_cast<uint32_t *>(workspace) : nullptr;
+    g.acc_ws = p.ws_bytes ? static_cast<char *>(workspace) + p.ws_counter_bytes : nullptr;
     g.M = M;
     g.N = N;
     g.K = K;
@@ -203,12 +219,59 @@ qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, cons
     g.nsplit = p.nsplit;
     g.phase_blocks = p.phase_blocks;
     g.out_type = out_type;
+    g.packed = p.packed;
     g.n_tiles = p.n_tiles;
     g.m_tiles = p.m_tiles;
     g.nw = p.nw;
     g.kw = p.kw;
-    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, g, p.lds_bytes,
+    return g;
+}
+
+qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, const float *x_scales,
+                      const void *wq, const float *w_scales, void *y, qlin_out_type out_type,
+                      const qlin_config *cfg, void *workspace, size_t ws_bytes, void *stream) {
+    qlin_config c;
+    Plan p;
+    qlin_status st = check_gemm(fmt, M, N, K, x_scales, wq, w_scales, y, out_type, cfg, workspace,
+                                ws_bytes, false, &c, &p);
+    if (st != QLIN_OK) return st;
+    if (!xq) return QLIN_ERR_INVALID_ARG;
+    if (!aligned16(xq)) return QLIN_ERR_ALIGNMENT;
+    if (M == 0) return QLIN_OK;
+    GemmLaunch g = launch_args(p, M, N, K, wq, w_scales, y, out_type, workspace);
+    g.xq = static_cast<const uint8_t *>(xq);
+    g.xs = x_scales;
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, false, g, p.lds_bytes,
                                   static_cast<hipStream_t>(stream)));
+}
+
+qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
+                        float *x_scales, const void *wq, const float *w_scales, void *y,
+                        qlin_out_type out_type, const qlin_config *cfg, void *workspace,
+                        size_t ws_bytes, void *stream) {
+    qlin_config c;
+    Plan p;
+    qlin_status st = check_gemm(fmt, M, N, K, x_scales, wq, w_scales, y, out_type, cfg, workspace,
+                                ws_bytes, true, &c, &p);
+    if (st != QLIN_OK) return st;
+    if (!x || !xq) return QLIN_ERR_INVALID_ARG;
+    if (ldx < K || ldx % 8 != 0) return QLIN_ERR_ALIGNMENT;
+    if (!aligned16(x) || !aligned16(xq)) return QLIN_ERR_ALIGNMENT;
+    if (M == 0) return QLIN_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GemmLaunch g = launch_args(p, M, N, K, wq, w_scales, y, out_type, workspace);
+    if (p.fuse) {
+        g.x = static_cast<const uint16_t *>(x);
+        g.ldx = ldx;
+        g.xq_out = static_cast<uint8_t *>(xq);
+        g.xs_out = x_scales;
+    } else {
+        st = hip_status(launch_quant_act(fmt, M, K, x, ldx, xq, x_scales, s));
+        if (st != QLIN_OK) return st;
+        g.xq = static_cast<const uint8_t *>(xq);
+        g.xs = x_scales;
+    }
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, p.fuse, g, p.lds_bytes, s));
 }
 
 struct qlin_graph_s {

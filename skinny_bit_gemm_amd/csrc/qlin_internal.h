@@ -18,12 +18,17 @@ constexpr int kMaxSplit = 64;
 
 // Everything a GEMM launch needs, resolved on the host.
 struct GemmLaunch {
-    const uint8_t *xq;
+    const uint8_t *xq;   // activation codes and scales (unfused path)
     const float *xs;
+    const uint16_t *x;   // fused path: bf16 activations [M][ldx] ...
+    int64_t ldx;
+    uint8_t *xq_out;     // ... and where the codes and scales it makes go
+    float *xs_out;
     const uint8_t *wq;
     const float *wsc;
     void *y;
-    void *acc_ws;        // split-K partial sums [M][N] (int32 or fp32), zero between calls
+    void *acc_ws;        // split-K: packed int64 sums [M][N] (zero between calls), or
+                         // per-partition slices [nsplit][M][N] of int32 / fp32
     uint32_t *counters;  // split-K arrival counters, one per output tile, zero between calls
     int M, N, K;
     int nkb;             // K blocks of 128 (last one may be partial)
@@ -31,6 +36,7 @@ struct GemmLaunch {
     int nsplit;          // effective number of partitions (grid z)
     int phase_blocks;    // K blocks of activations staged in LDS at once
     int out_type;
+    int packed;          // split-K through packed 64-bit integer atomics (exact formats)
     int n_tiles, m_tiles;
     int nw, kw;          // waves along N and along K
 };
@@ -41,12 +47,16 @@ struct Plan {
     int nkb, kb_per_split, nsplit, phase_blocks;
     int n_tiles, m_tiles;
     size_t lds_bytes;
-    size_t ws_bytes;      // workspace bytes (0 without split)
-    size_t ws_acc_bytes;  // of which partial sums
+    int packed;           // split-K reduction through packed 64-bit atomics
+    int fuse;             // activation quantization inside the GEMM kernel
+    size_t ws_bytes;          // workspace bytes (0 without split)
+    size_t ws_counter_bytes;  // of which arrival counters (the rest: sums)
 };
 
 // Fills *plan; returns QLIN_OK or the reason the schedule is invalid.
-qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &cfg, Plan *plan);
+// `fused`: planned for qlin_linear (cfg.fuse_quant applies) or qlin_gemm.
+qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &cfg, bool fused,
+                      Plan *plan);
 
 // Host-side selection table (qlin_table.cpp).
 qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out, bool *found);
@@ -59,8 +69,8 @@ hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, v
                             float *xs, hipStream_t s);
 hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, float *ws,
                                hipStream_t s);
-hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, const GemmLaunch &g,
+hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, bool fuse, const GemmLaunch &g,
                        size_t lds_bytes, hipStream_t s);
-bool gemm_variant_exists(int fmt, int tile_m, int nr);
+bool gemm_variant_exists(int fmt, int tile_m, int nr, bool fuse);
 
 }  // namespace qlin

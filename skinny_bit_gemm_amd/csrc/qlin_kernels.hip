@@ -342,16 +342,39 @@ __device__ __forceinline__ void wait_memory_idle() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int FMT, bool SWAP, int MT, int NR, int PF>
+// Activation staging of the fused path: 16 consecutive bf16 values of one
+// token row become 16 codes (one uint4).  For the block format the 8 lanes
+// that share a 128-wide group (lanes 8j .. 8j+7 of a wave) first reduce the
+// group's amax.  Returns the codes; *gscale receives the group scale.
+template <int FMT>
+__device__ __forceinline__ uint4 quant16(const uint16_t *src, float row_scale, float *gscale) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(src);
+    const uint4 b = *reinterpret_cast<const uint4 *>(src + 8);
+    float s = row_scale;
+    if constexpr (FMT == FMT_BLOCK) {
+        float amax = fmaxf(absmax8(a), absmax8(b));
+#pragma unroll
+        for (int o = 4; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+        s = amax == 0.0f ? 0.0f : amax / 448.0f;
+        *gscale = s;
+    }
+    const uint2 lo = quant8<FMT>(a, s);
+    const uint2 hi = quant8<FMT>(b, s);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+template <int FMT, bool SWAP, int MT, int NR, int PF, bool FUSE>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     typedef typename AccT<FMT>::type acc_t;
     typedef typename AccT<FMT>::scalar acc_s;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
+    __shared__ float s_rowscale[16 * MT];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nthreads = blockDim.x;
+    const int nwaves = nthreads >> 6;
     const int nw = wave % g.nw, kw = wave / g.nw;
     const int TN = 16 * NR * g.nw;
     const int n_tile0 = blockIdx.x * TN;
@@ -362,6 +385,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     const int r16 = lane & 15, quarter = lane >> 4;
     const int G = (K + kGroup - 1) / kGroup;
     const int R = min(16 * MT, M - m0);   // token rows that exist in this tile
+    // fused path: the first column of workgroups also stores the codes and
+    // scales it produces (every workgroup of a row of tiles produces the same)
+    const bool writer = FUSE && blockIdx.x == 0;
 
     int nsub[NR];
     const uint8_t *wrow[NR];
@@ -378,27 +404,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[r][mt] = acc_t{0, 0, 0, 0};
 
-    // Per-channel formats: the epilogue's token and channel scales are
-    // requested now, so their latency hides behind the weight stream.
-    // Swap-AB lanes need one token scale and 4 channel scales per sub-tile,
-    // Standard lanes 4 token scales and one channel scale.
+    // Per-channel formats: the epilogue's channel scales are requested now,
+    // so their latency hides behind the weight stream (token scales too,
+    // unless the fused path computes them below).  Swap-AB lanes need one
+    // token scale and 4 channel scales per sub-tile, Standard lanes 4 token
+    // scales and one channel scale.
     float pre_sa[MT][SWAP ? 1 : 4], pre_sw[NR][SWAP ? 4 : 1];
+    auto token_of = [&](int mt, int i) { return SWAP ? m0 + mt * 16 + r16 : m0 + mt * 16 + 4 * quarter + i; };
     if constexpr (FMT != FMT_BLOCK) {
-        if (g.nsplit == 1) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int i = 0; i < (SWAP ? 4 : 1); ++i) {
+                const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
+                pre_sw[r][i] = g.wsc[min(n, N - 1)];
+            }
+        if constexpr (!FUSE) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < (SWAP ? 1 : 4); ++i) {
-                    const int m = SWAP ? m0 + mt * 16 + r16 : m0 + mt * 16 + 4 * quarter + i;
-                    pre_sa[mt][i] = g.xs[min(m, M - 1)];
-                }
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-#pragma unroll
-                for (int i = 0; i < (SWAP ? 4 : 1); ++i) {
-                    const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
-                    pre_sw[r][i] = g.wsc[min(n, N - 1)];
-                }
+                for (int i = 0; i < (SWAP ? 1 : 4); ++i) pre_sa[mt][i] = g.xs[min(token_of(mt, i), M - 1)];
         }
     }
 
@@ -428,6 +453,29 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             if (b < nblk) issue(wbuf[p], wsbuf[p], pb0 + b);
         }
         if (pb0 != kb_begin) __syncthreads();
+        float *s_scale = reinterpret_cast<float *>(smem + (size_t)g.phase_blocks * kGroup * R);
+
+        if constexpr (FUSE && FMT != FMT_BLOCK) {
+            // per-token scales need the whole row: one wave per token row
+            // finds its amax over all of K (the rows are small and shared by
+            // every workgroup, so they come from L2)
+            if (pb0 == kb_begin) {
+                for (int row = wave; row < R; row += nwaves) {
+                    const uint16_t *xr = g.x + (int64_t)(m0 + row) * g.ldx;
+                    float amax = 0.0f;
+                    for (int c = lane; c < K / 8; c += 64)
+                        amax = fmaxf(amax, absmax8(*reinterpret_cast<const uint4 *>(xr + c * 8)));
+                    amax = wave_max(amax);
+                    if (lane == 0) {
+                        const float sc = amax == 0.0f ? 0.0f : amax / qmax_of<FMT>();
+                        s_rowscale[row] = sc;
+                        if (writer && blockIdx.z == 0) g.xs_out[m0 + row] = sc;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+
         // stage the activation codes of this phase: [block][half][quarter][row][16B]
         const int items = R * nblk * 8;
         for (int it = threadIdx.x; it < items; it += nthreads) {
@@ -437,11 +485,25 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             const int row = rest / nblk;
             const int k = (pb0 + b) * kGroup + c * 16;
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (k < K) v = *reinterpret_cast<const uint4 *>(g.xq + (int64_t)(m0 + row) * K + k);
+            if constexpr (FUSE) {
+                float gs = 0.0f;
+                if (k < K) {
+                    v = quant16<FMT>(g.x + (int64_t)(m0 + row) * g.ldx + k,
+                                     FMT == FMT_BLOCK ? 0.0f : s_rowscale[row], &gs);
+                    if (writer) *reinterpret_cast<uint4 *>(g.xq_out + (int64_t)(m0 + row) * K + k) = v;
+                }
+                if constexpr (FMT == FMT_BLOCK) {
+                    if (c == 0) {
+                        s_scale[b * R + row] = gs;
+                        if (writer) g.xs_out[(int64_t)(m0 + row) * G + pb0 + b] = gs;
+                    }
+                }
+            } else {
+                if (k < K) v = *reinterpret_cast<const uint4 *>(g.xq + (int64_t)(m0 + row) * K + k);
+            }
             *reinterpret_cast<uint4 *>(smem + (((b * 2 + (c & 1)) * 4 + (c >> 1)) * R + row) * 16) = v;
         }
-        float *s_scale = reinterpret_cast<float *>(smem + (size_t)g.phase_blocks * kGroup * R);
-        if constexpr (FMT == FMT_BLOCK) {
+        if constexpr (FMT == FMT_BLOCK && !FUSE) {
             for (int it = threadIdx.x; it < nblk * R; it += nthreads) {
                 const int row = it % R, b = it / R;
                 s_scale[b * R + row] = g.xs[(int64_t)(m0 + row) * G + pb0 + b];
@@ -508,6 +570,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         }
     }
 
+    if constexpr (FUSE && FMT != FMT_BLOCK) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < (SWAP ? 1 : 4); ++i) {
+                const int row = token_of(mt, i) - m0;
+                pre_sa[mt][i] = row < R ? s_rowscale[row] : 0.0f;
+            }
+    }
+
     // add the partial sums of the kw waves of each column through LDS
     if (g.kw > 1) {
         __syncthreads();
@@ -530,10 +602,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         }
     }
 
-    // value written for output (m, n) from a raw sum v
-    auto finish = [&](acc_s v, int m, int n) -> float {
-        if constexpr (FMT == FMT_BLOCK) return (float)v;
-        else return ((float)v * g.xs[m]) * g.wsc[n];
+    // output value from a total t (scaled sum for the block format, raw sum
+    // otherwise) for accumulator element (r, mt, i) of this lane
+    auto scaled = [&](float t, int r, int mt, int i) -> float {
+        if constexpr (FMT == FMT_BLOCK) return t;
+        else return (t * pre_sa[mt][SWAP ? 0 : i]) * pre_sw[r][SWAP ? i : 0];
+    };
+    auto store1 = [&](int64_t idx, float o, int raw) {
+        if (g.out_type == QLIN_OUT_I32_ACC) static_cast<int *>(g.y)[idx] = raw;
+        else if (g.out_type == QLIN_OUT_F32_ACC) static_cast<float *>(g.y)[idx] = o;
+        else static_cast<uint16_t *>(g.y)[idx] = (uint16_t)bf16_bits(o);
     };
 
     if (g.nsplit == 1) {
@@ -554,10 +632,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                     } else {
                         float o[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            if constexpr (FMT == FMT_BLOCK) o[i] = acc[r][mt][i];
-                            else o[i] = ((float)acc[r][mt][i] * pre_sa[mt][0]) * pre_sw[r][i];
-                        }
+                        for (int i = 0; i < 4; ++i) o[i] = scaled((float)acc[r][mt][i], r, mt, i);
                         if (g.out_type == QLIN_OUT_F32_ACC) {
                             *reinterpret_cast<float4 *>(static_cast<float *>(g.y) + (int64_t)m * N + n) =
                                 make_float4(o[0], o[1], o[2], o[3]);
@@ -573,16 +648,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                     for (int i = 0; i < 4; ++i) {
                         const int m = m0 + mt * 16 + 4 * quarter + i;
                         if (m >= M) continue;
-                        const int64_t idx = (int64_t)m * N + n;
-                        float o;
-                        if constexpr (FMT == FMT_BLOCK) o = acc[r][mt][i];
-                        else o = ((float)acc[r][mt][i] * pre_sa[mt][i]) * pre_sw[r][0];
-                        if (g.out_type == QLIN_OUT_I32_ACC)
-                            static_cast<int *>(g.y)[idx] = (int)acc[r][mt][i];
-                        else if (g.out_type == QLIN_OUT_F32_ACC)
-                            static_cast<float *>(g.y)[idx] = o;
-                        else
-                            static_cast<uint16_t *>(g.y)[idx] = (uint16_t)bf16_bits(o);
+                        store1((int64_t)m * N + n, scaled((float)acc[r][mt][i], r, mt, i), (int)acc[r][mt][i]);
                     }
                 }
             }
@@ -590,11 +656,61 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         return;
     }
 
-    // Split-K (the partials of each partition are added into a zeroed
-    // workspace): atomically add this partition's sums, count the arrival;
-    // the last partition to arrive for this tile writes the output from the
-    // totals and re-zeroes the workspace and the counter.
-    acc_s *ws = static_cast<acc_s *>(g.acc_ws);
+    // Split-K: the partitions' partial sums are combined in one of two ways.
+    //
+    // Packed (exact formats: int8, and fp8 with per-channel scales): one
+    // returning 64-bit atomic per output.  A partition's sum is an integer:
+    // int8 sums are int32, and fp8 products are whole multiples of 2^-18, so
+    // every fp32 partial sum of them is too and p * 2^18 converts exactly.
+    // Each partition adds p + 2^52 to a zeroed element; while |sum| < 2^51
+    // the value returned, old = S + c * 2^52, gives the number c of
+    // partitions that came before and their exact sum S.  The partition that
+    // sees c = nsplit - 1 holds the total, writes the output and zeroes the
+    // element.  One round trip, and the result does not depend on the order.
+    if constexpr (FMT != FMT_BLOCK) {
+        if (g.packed) {
+            if (kw != 0) return;
+            unsigned long long *ws64 = static_cast<unsigned long long *>(g.acc_ws);
+            const unsigned long long kUnit = 1ull << 52, kHalf = 1ull << 51;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (nsub[r] >= N) continue;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = token_of(mt, i);
+                        const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
+                        if (m >= M) continue;
+                        const int64_t idx = (int64_t)m * N + n;
+                        long long v;
+                        if constexpr (FMT == FMT_I8) v = (long long)acc[r][mt][i];
+                        else v = (long long)(acc[r][mt][i] * 262144.0f);
+                        const unsigned long long old = __hip_atomic_fetch_add(
+                            &ws64[idx], (unsigned long long)(v + (long long)kUnit), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+                        const unsigned long long before = (old + kHalf) >> 52;
+                        if (before != (unsigned long long)(g.nsplit - 1)) continue;
+                        const long long total = (long long)(old - before * kUnit) + v;
+                        float t;
+                        if constexpr (FMT == FMT_I8) t = (float)total;
+                        else t = (float)((double)total * (1.0 / 262144.0));
+                        store1(idx, scaled(t, r, mt, i), (int)total);
+                        __hip_atomic_store(&ws64[idx], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+            }
+            return;
+        }
+    }
+
+    // Slices (any format): each partition stores its partial sums into its
+    // own slice of the workspace with device-coherent stores, waits until
+    // they are acknowledged, and counts its arrival for the tile.  The last
+    // partition to arrive adds the slices in partition order (so the result
+    // is deterministic), writes the output, and zeroes the slices and the
+    // counter.
+    acc_s *part = static_cast<acc_s *>(g.acc_ws);
+    const int64_t slice = (int64_t)M * N;
     if (kw == 0) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -603,11 +719,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int m = SWAP ? m0 + mt * 16 + r16 : m0 + mt * 16 + 4 * quarter + i;
+                    const int m = token_of(mt, i);
                     const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
                     if (m < M)
-                        __hip_atomic_fetch_add(&ws[(int64_t)m * N + n], acc[r][mt][i], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&part[blockIdx.z * slice + (int64_t)m * N + n],
+                                           (acc_s)acc[r][mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
         }
     }
@@ -626,14 +742,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         const int m = m0 + e / tn;
         const int n = n_tile0 + e % tn;
         const int64_t idx = (int64_t)m * N + n;
-        const acc_s v = __hip_atomic_exchange(&ws[idx], (acc_s)0, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-        if (g.out_type == QLIN_OUT_I32_ACC)
-            static_cast<int *>(g.y)[idx] = (int)v;
-        else if (g.out_type == QLIN_OUT_F32_ACC)
-            static_cast<float *>(g.y)[idx] = finish(v, m, n);
-        else
-            static_cast<uint16_t *>(g.y)[idx] = (uint16_t)bf16_bits(finish(v, m, n));
+        acc_s v = 0;
+        for (int z = 0; z < g.nsplit; ++z)
+            v += __hip_atomic_load(&part[z * slice + idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int z = 0; z < g.nsplit; ++z)   // leave the workspace zero
+            __hip_atomic_store(&part[z * slice + idx], (acc_s)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float o;
+        if constexpr (FMT == FMT_BLOCK) o = v;
+        else if constexpr (FUSE) o = ((float)v * s_rowscale[m - m0]) * g.wsc[n];
+        else o = ((float)v * g.xs[m]) * g.wsc[n];
+        store1(idx, o, (int)v);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&g.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -687,30 +805,38 @@ hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, 
 
 typedef void (*gemm_fn)(GemmLaunch);
 
+// prefetch depth: 8 blocks of 16 weight rows in flight per wave (4 for NR = 4)
+#define QLIN_PF(NR_) (NR_ >= 4 ? 2 : 8 / NR_)
+
 template <int FMT, bool SWAP>
-static gemm_fn pick(int tile_m, int nr) {
-#define QLIN_PICK(MT_, NR_) \
-    if (tile_m == 16 * MT_ && nr == NR_) return gemm_kernel<FMT, SWAP, MT_, NR_, (NR_ >= 4 ? 2 : 4 / NR_ * 2)>;
-    QLIN_PICK(1, 1) QLIN_PICK(1, 2) QLIN_PICK(1, 4)
-    QLIN_PICK(2, 1) QLIN_PICK(2, 2) QLIN_PICK(2, 4)
+static gemm_fn pick(int tile_m, int nr, bool fuse) {
+#define QLIN_PICK(MT_, NR_, FUSE_)                                 \
+    if (tile_m == 16 * MT_ && nr == NR_ && fuse == FUSE_)          \
+        return gemm_kernel<FMT, SWAP, MT_, NR_, QLIN_PF(NR_), FUSE_>;
+    QLIN_PICK(1, 1, false) QLIN_PICK(1, 2, false) QLIN_PICK(1, 4, false)
+    QLIN_PICK(2, 1, false) QLIN_PICK(2, 2, false) QLIN_PICK(2, 4, false)
+    QLIN_PICK(1, 1, true) QLIN_PICK(1, 2, true) QLIN_PICK(1, 4, true)
 #undef QLIN_PICK
     return nullptr;
 }
 
-static gemm_fn pick_any(int fmt, bool swap, int tile_m, int nr) {
+static gemm_fn pick_any(int fmt, bool swap, int tile_m, int nr, bool fuse) {
     switch (fmt) {
-    case FMT_FP8: return swap ? pick<FMT_FP8, true>(tile_m, nr) : pick<FMT_FP8, false>(tile_m, nr);
-    case FMT_I8: return swap ? pick<FMT_I8, true>(tile_m, nr) : pick<FMT_I8, false>(tile_m, nr);
-    case FMT_BLOCK: return swap ? pick<FMT_BLOCK, true>(tile_m, nr) : pick<FMT_BLOCK, false>(tile_m, nr);
+    case FMT_FP8: return swap ? pick<FMT_FP8, true>(tile_m, nr, fuse) : pick<FMT_FP8, false>(tile_m, nr, fuse);
+    case FMT_I8: return swap ? pick<FMT_I8, true>(tile_m, nr, fuse) : pick<FMT_I8, false>(tile_m, nr, fuse);
+    case FMT_BLOCK:
+        return swap ? pick<FMT_BLOCK, true>(tile_m, nr, fuse) : pick<FMT_BLOCK, false>(tile_m, nr, fuse);
     }
     return nullptr;
 }
 
-bool gemm_variant_exists(int fmt, int tile_m, int nr) { return pick_any(fmt, false, tile_m, nr) != nullptr; }
+bool gemm_variant_exists(int fmt, int tile_m, int nr, bool fuse) {
+    return pick_any(fmt, false, tile_m, nr, fuse) != nullptr;
+}
 
-hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, const GemmLaunch &g,
+hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, bool fuse, const GemmLaunch &g,
                        size_t lds_bytes, hipStream_t s) {
-    gemm_fn f = pick_any(fmt, swap, tile_m, nr);
+    gemm_fn f = pick_any(fmt, swap, tile_m, nr, fuse);
     if (!f) return hipErrorInvalidValue;
     const dim3 grid(g.n_tiles, g.m_tiles, g.nsplit);
     const dim3 block(64 * g.nw * g.kw);

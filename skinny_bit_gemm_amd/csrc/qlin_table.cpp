@@ -12,6 +12,7 @@
 // Table format (text, '#' starts a comment):
 //   qlin-table <abi version> <gfx arch>
 //   <format> <N> <K> <M bucket> <swap_ab> <split_k> <tile_m> <tile_n> <waves> <k_waves>
+//            <reduce> <fuse_quant>
 // with <format> one of fp8_dynamic, w8a8_int8, block_fp8.
 #include <dlfcn.h>
 
@@ -88,18 +89,18 @@ qlin_status parse_file(const std::string &path, std::map<Key, qlin_config> *out)
             continue;
         }
         char fmt_s[64];
-        int N, K, M, swap, split, tm, tn, waves, kwv;
+        int N, K, M, swap, split, tm, tn, waves, kwv, red, fuse;
         char extra[8];
-        const int n = sscanf(line, "%63s %d %d %d %d %d %d %d %d %d %7s", fmt_s, &N, &K, &M, &swap,
-                             &split, &tm, &tn, &waves, &kwv, extra);
+        const int n = sscanf(line, "%63s %d %d %d %d %d %d %d %d %d %d %d %7s", fmt_s, &N, &K, &M,
+                             &swap, &split, &tm, &tn, &waves, &kwv, &red, &fuse, extra);
         const int fmt = parse_format(fmt_s);
-        if (n != 10 || fmt < 0) {
+        if (n != 12 || fmt < 0) {
             st = QLIN_ERR_TABLE;
             break;
         }
-        qlin_config c{swap, split, tm, tn, waves, kwv};
+        qlin_config c{swap, split, tm, tn, waves, kwv, red, fuse};
         Plan p;
-        if (token_bucket(M) != M || make_plan((qlin_format)fmt, M, N, K, c, &p) != QLIN_OK) {
+        if (token_bucket(M) != M || make_plan((qlin_format)fmt, M, N, K, c, true, &p) != QLIN_OK) {
             st = QLIN_ERR_TABLE;
             break;
         }
@@ -155,9 +156,9 @@ qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out,
 // follows the pages' example heuristic of dispatching to Swap-AB below 32
 // tokens (section "Kernel Implementation") and chooses a split so that the
 // grid has about four workgroups per compute unit, with at least one K block
-// per wave.
+// per wave; small token counts quantize inside the GEMM and combine exact
+// partitions with packed atomics.
 void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
-    (void)fmt;
     qlin_config c;
     c.tile_m = M <= 16 ? 16 : 32;
     c.swap_ab = M < 32 ? 1 : 0;
@@ -172,6 +173,9 @@ void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
            nkb / (split * 2) >= c.k_waves)
         split *= 2;
     c.split_k = split;
+    const bool exact = fmt == QLIN_W8A8_INT8 || (fmt == QLIN_FP8_DYNAMIC && K <= 40960);
+    c.reduce = exact && M <= 8 ? 1 : 0;
+    c.fuse_quant = M <= 4 && c.tile_m == 16 ? 1 : 0;
     *out = c;
 }
 

@@ -7,9 +7,11 @@ range gets its own configuration) and "Enable CUDA Graph for Autotuner
 Benchmarking" (candidates are timed the way they run in production, under
 graph replay).  Here the search is exhaustive over a fixed candidate grid
 (schedule, tile, split factor, wave layout); each candidate is timed as a
-hipGraph of back-to-back launches over distinct weight copies (>= 1 GiB in
-total, so the Infinity Cache cannot hold them), coarse pass first, then the
-best few again with more replays.
+hipGraph of back-to-back layers (qlin_linear: quantize + GEMM) over distinct
+weight copies (>= 1 GiB in total, so the Infinity Cache cannot hold them).
+A coarse pass over the schedule grid, then the best few with each split-K
+reduction and with the quantization fused or not, then the best of those
+again with more replays.
 
 Usage:
   python -m skinny_bit_gemm_amd.tune --shape fp8_dynamic,4096,2048 ... \\
@@ -36,7 +38,13 @@ TILES = [(16, 1, 1), (16, 2, 2), (16, 4, 4), (16, 8, 8), (32, 1, 1), (32, 2, 2),
 SPLITS = [1, 2, 3, 4, 6, 8, 12, 16, 24, 32]
 
 
+def exact_format(fmt, K):
+    return fmt == q.QLIN_W8A8_INT8 or (fmt == q.QLIN_FP8_DYNAMIC and K <= 40960)
+
+
 def candidates(fmt, M, N, K):
+    """Base grid: schedule, tile, split and wave layout (slice reduction,
+    separate quantize kernel)."""
     nkb = -(-K // 128)
     seen = set()
     out = []
@@ -49,7 +57,7 @@ def candidates(fmt, M, N, K):
                 key = (swap, tn, waves, kw, kbs)
                 if key in seen or kbs < kw:
                     continue
-                c = q.make_config(swap, eff, tile_m, tn, waves, kw)
+                c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, 0)
                 if q.qlin_validate_config(fmt, M, N, K, c) != 0:
                     continue
                 wgs = -(-N // tn) * -(-M // tile_m) * eff
@@ -60,8 +68,21 @@ def candidates(fmt, M, N, K):
     return out
 
 
+def variants(fmt, M, N, K, c):
+    """The same schedule with each split-K reduction and quantize placement."""
+    out = []
+    reds = [0, 1] if (c.split_k > 1 and exact_format(fmt, K)) else [0]
+    fuses = [0, 1] if c.tile_m == 16 else [0]
+    for r in reds:
+        for f in fuses:
+            v = q.make_config(c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves, r, f)
+            if q.qlin_validate_config(fmt, M, N, K, v) == 0:
+                out.append(v)
+    return out
+
+
 class Bench:
-    """Device buffers for timing one (fmt, M, N, K) point."""
+    """Device buffers for timing one (fmt, M, N, K) linear layer."""
 
     def __init__(self, fmt, M, N, K, min_bytes=1 << 30):
         import torch
@@ -79,24 +100,30 @@ class Bench:
             return t
         self.W = [codes((N, K)) for _ in range(self.R)]
         self.ws = torch.rand(q.scales_shape(fmt, N, K, True), device=dev, generator=g) * 1e-2
-        self.xq = codes((M, K))
-        self.xs = torch.rand(q.scales_shape(fmt, M, K, False), device=dev, generator=g)
+        self.x = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
+        self.xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        self.xs = torch.empty(q.scales_shape(fmt, M, K, False), dtype=torch.float32, device=dev)
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         self.stream = torch.cuda.Stream()
+        self.work = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+
+    def _call(self, cfg, w, st):
+        q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, w, self.ws,
+                      self.y, q.QLIN_OUT_BF16, cfg, self.work, stream=st)
 
     def time(self, cfg, replays=3):
+        """Mean time of one linear (quantize + GEMM) under graph replay."""
         torch = self.torch
         nb = q.qlin_workspace_bytes(self.fmt, self.M, self.N, self.K, cfg)
-        work = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+        if nb > self.work.numel():
+            self.work = torch.zeros(nb, dtype=torch.uint8, device="cuda")
         st = self.stream
         with torch.cuda.stream(st):
-            q.qlin_gemm(self.fmt, self.M, self.N, self.K, self.xq, self.xs, self.W[0], self.ws,
-                        self.y, q.QLIN_OUT_BF16, cfg, work, stream=st)
+            self._call(cfg, self.W[0], st)
             q.qlin_graph_begin(st)
             try:
                 for w in self.W:
-                    q.qlin_gemm(self.fmt, self.M, self.N, self.K, self.xq, self.xs, w, self.ws,
-                                self.y, q.QLIN_OUT_BF16, cfg, work, stream=st)
+                    self._call(cfg, w, st)
             finally:
                 gr = q.qlin_graph_end(st)
             q.qlin_graph_launch(gr, st)
@@ -121,24 +148,21 @@ def variant_class(c):
     return "swap_ab" if c.swap_ab else "standard"
 
 
-def tune_point(fmt, M, N, K, keep=6):
+def tune_point(fmt, M, N, K, keep=10, final=5):
     b = Bench(fmt, M, N, K)
-    cands = candidates(fmt, M, N, K)
-    coarse = []
-    for c in cands:
-        coarse.append((b.time(c, replays=1), c))
-    coarse.sort(key=lambda t: t[0])
-    fine = []
-    for _, c in coarse[:keep]:
-        fine.append((b.time(c, replays=5), c))
-    fine.sort(key=lambda t: t[0])
+    base = candidates(fmt, M, N, K)
+    coarse = sorted(((b.time(c, replays=1), c) for c in base), key=lambda t: t[0])
     best_by_class = {}
     for t, c in coarse:
-        cls = variant_class(c)
-        if cls not in best_by_class:
-            best_by_class[cls] = (t, c)
+        best_by_class.setdefault(variant_class(c), (t, c))
+    expanded = []
+    for _, c in coarse[:keep]:
+        for v in variants(fmt, M, N, K, c):
+            expanded.append((b.time(v, replays=2), v))
+    expanded.sort(key=lambda t: t[0])
+    fine = sorted(((b.time(c, replays=5), c) for _, c in expanded[:final]), key=lambda t: t[0])
     b.free()
-    return fine[0], best_by_class, len(cands)
+    return fine[0], best_by_class, len(base) + len(expanded)
 
 
 def algorithmic_bytes(fmt, M, N, K):
@@ -164,7 +188,7 @@ def main(argv=None):
         with open(args.out) as f:
             for line in f:
                 p = line.split("#")[0].split()
-                if len(p) == 10:
+                if len(p) == 12:
                     entries[(p[0], int(p[1]), int(p[2]), int(p[3]))] = p[4:]
     report = []
     t_start = time.time()
@@ -175,7 +199,7 @@ def main(argv=None):
             (t, c), by_class, n = tune_point(fmt, M, N, K)
             gbs = algorithmic_bytes(fmt, M, N, K) / t / 1e3
             entries[(fname, N, K, M)] = [str(v) for v in (c.swap_ab, c.split_k, c.tile_m, c.tile_n,
-                                                         c.waves, c.k_waves)]
+                                                         c.waves, c.k_waves, c.reduce, c.fuse_quant)]
             rec = {"fmt": fname, "N": N, "K": K, "M": M, "us": round(t, 3), "GBps": round(gbs, 1),
                    "cfg": c.as_dict(), "candidates": n,
                    "best_by_class": {k: {"us": round(v[0], 3), "cfg": v[1].as_dict()}
@@ -188,7 +212,9 @@ def main(argv=None):
     with open(args.out, "w") as f:
         f.write(f"qlin-table {q.qlin_abi_version()} gfx950\n")
         f.write("# measured on MI355X by skinny_bit_gemm_amd.tune (hipGraph replay, rotating weights)\n")
-        f.write("# format N K M swap_ab split_k tile_m tile_n waves k_waves\n")
+        f.write("# format N K M swap_ab split_k tile_m tile_n waves k_waves reduce fuse_quant\n")
+        f.write("# (times are of the whole layer, quantize + GEMM; best_by_class in the report\n"
+                "#  compares schedules with a separate quantize kernel and slice reduction)\n")
         for k in sorted(entries):
             f.write(" ".join([k[0], str(k[1]), str(k[2]), str(k[3])] + entries[k]) + "\n")
     if args.report:

@@ -74,3 +74,22 @@ def y_to_numpy(y: torch.Tensor, out_type=q.QLIN_OUT_BF16) -> np.ndarray:
 
 def as_u8(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().view(np.uint8)
+
+
+def gpu_linear(fmt, x_bits, wq, ws, N, cfg=None, out_type=q.QLIN_OUT_BF16, workspace=None, ldx=None):
+    """The whole layer through qlin_linear: returns (xq, xs, y)."""
+    M, K = x_bits.shape
+    ldx = K if ldx is None else ldx
+    padded = np.zeros((M, ldx), dtype=np.uint16)
+    padded[:, :K] = x_bits
+    xd = to_dev_bf16(padded)
+    xq = torch.full((M, K), 0x55, dtype=torch.uint8, device=DEV)
+    xs = torch.full(q.scales_shape(fmt, M, K, False), -1.0, dtype=torch.float32, device=DEV)
+    dt = {q.QLIN_OUT_BF16: torch.int16, q.QLIN_OUT_F32_ACC: torch.float32,
+          q.QLIN_OUT_I32_ACC: torch.int32}[out_type]
+    y = torch.full((M, N), -1, dtype=dt, device=DEV)
+    if workspace is None:
+        workspace = workspace_for(fmt, M, N, K, cfg)
+    q.qlin_linear(fmt, M, N, K, xd, ldx, xq, xs, wq, ws, y, out_type, cfg, workspace)
+    torch.cuda.synchronize()
+    return xq, xs, y

@@ -131,8 +131,8 @@ def write_table(tmp_path, body, header="qlin-table 1 gfx950"):
 
 def test_table_load_lookup_and_bucket_round_up(tmp_path):
     path = write_table(tmp_path, "# comment\n"
-                       "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n"
-                       "fp8_dynamic 1024 1024 32 0 4 32 32 4 4   # trailing comment\n")
+                       "fp8_dynamic 1024 1024 4 1 2 16 64 4 2 0 0\n"
+                       "fp8_dynamic 1024 1024 32 0 4 32 32 4 4 0 0   # trailing comment\n")
     assert q.qlin_load_table(path) == OK
     assert q.qlin_table_entries() == 2
     c = q.qlin_select_variant(FP8, 3, 1024, 1024)           # 3 -> bucket 4
@@ -142,7 +142,7 @@ def test_table_load_lookup_and_bucket_round_up(tmp_path):
 
 
 def test_strict_mode_missing_entry_is_an_error(tmp_path):
-    path = write_table(tmp_path, "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n")
+    path = write_table(tmp_path, "fp8_dynamic 1024 1024 4 1 2 16 64 4 2 0 0\n")
     assert q.qlin_load_table(path) == OK
     q.qlin_set_strict(True)
     with pytest.raises(q.QlinError) as e:
@@ -156,16 +156,18 @@ def test_strict_mode_missing_entry_is_an_error(tmp_path):
 
 
 @pytest.mark.parametrize("header,body", [
-    ("qlin-table 1 gfx942", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n"),     # wrong arch
-    ("qlin-table 2 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n"),     # wrong version
-    ("qlin-table 1 gfx950", "fp4 1024 1024 4 1 2 16 64 4 2\n"),             # unknown format
-    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 64 4\n"),       # short line
-    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 5 1 2 16 64 4 2\n"),     # 5 is no bucket
-    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 48 4 2\n"),     # invalid tile
+    ("qlin-table 1 gfx942", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2 0 0\n"),     # wrong arch
+    ("qlin-table 2 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2 0 0\n"),     # wrong version
+    ("qlin-table 1 gfx950", "fp4 1024 1024 4 1 2 16 64 4 2 0 0\n"),             # unknown format
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2 0\n"),   # short line
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 5 1 2 16 64 4 2 0 0\n"),     # 5 is no bucket
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 48 4 2 0 0\n"),     # invalid tile
+    ("qlin-table 1 gfx950", "block_fp8 1024 1024 4 1 2 16 64 4 2 1 0\n"),  # packed: exact formats only
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 32 1 2 32 64 4 2 0 1\n"),  # fused needs tile_m 16
     ("nonsense", ""),
 ])
 def test_corrupt_tables_are_rejected(tmp_path, header, body):
-    good = write_table(tmp_path, "fp8_dynamic 1024 1024 4 1 2 16 64 4 2\n")
+    good = write_table(tmp_path, "fp8_dynamic 1024 1024 4 1 2 16 64 4 2 0 0\n")
     assert q.qlin_load_table(good) == OK
     p = tmp_path / "bad.tbl"
     p.write_text(header + "\n" + body)

@@ -14,8 +14,8 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import (as_u8, gpu_gemm, gpu_quant_act, gpu_quant_weight, workspace_for,  # noqa: E402
-                  y_to_numpy)
+from _gpu import (as_u8, gpu_gemm, gpu_linear, gpu_quant_act, gpu_quant_weight,  # noqa: E402
+                  workspace_for, y_to_numpy)
 
 FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
 FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
@@ -29,8 +29,8 @@ def _gpu_ready():
     oracle.build()
 
 
-def cfg(swap=0, split=1, tile_m=16, tile_n=32, waves=4, k_waves=4):
-    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves)
+def cfg(swap=0, split=1, tile_m=16, tile_n=32, waves=4, k_waves=4, reduce=0, fuse=0):
+    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves, reduce, fuse)
 
 
 # schedules every format is checked with: Standard, Swap-AB, Split-K (with
@@ -46,6 +46,12 @@ SCHEDULES = {
     "nw4": cfg(0, 3, 16, 128, 8, 2),
     "nr4": cfg(1, 2, 32, 64, 1, 1),
     "w8k8": cfg(0, 1, 16, 16, 8, 8),
+}
+# the same with packed-atomic reduction (exact formats only)
+PACKED = {
+    "packed4_swap": cfg(1, 4, 16, 64, 4, 1, reduce=1),
+    "packed16": cfg(1, 16, 32, 16, 2, 2, reduce=1),
+    "packed3_nw4": cfg(0, 3, 16, 128, 8, 2, reduce=1),
 }
 
 
@@ -89,6 +95,84 @@ def test_schedules_match_oracle(fmt, sched):
     x = wl.activations(fmt, N, K, M)
     w = wl.random_weights(N, K, 31)
     check_linear(fmt, M, N, K, x, w, sched)
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
+@pytest.mark.parametrize("sched", list(PACKED))
+@pytest.mark.parametrize("M", [1, 7, 32])
+def test_packed_reduction_matches_oracle(fmt, sched, M):
+    N, K = 512, 2048 + 16
+    x = wl.activations(fmt, N, K, M) if K % 128 == 0 else wl.random_bf16((M, K), 3)
+    w = wl.random_weights(N, K, 32)
+    check_linear(fmt, M, N, K, x, w, PACKED[sched])
+
+
+def check_layer(fmt, M, N, K, x, w, c, ldx=None):
+    """qlin_linear (quantize + GEMM, fused or not) against the oracle."""
+    print(f"[layer] fmt={fmt} M={M} N={N} K={K} cfg={c}", flush=True)
+    qw_o, sw_o = oracle.quant_weight(fmt, w)
+    qa_o, sa_o, ref = oracle.linear(fmt, x, qw_o, sw_o)
+    wq, ws = gpu_quant_weight(fmt, w)
+    xq, xs, y = gpu_linear(fmt, x, wq, ws, N, c, ldx=ldx)
+    assert np.array_equal(as_u8(xq), qa_o), "activation codes differ"
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa_o.view(np.uint32)), "activation scales differ"
+    ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
+    assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
+    if fmt == wl.W8A8_INT8:
+        _, acc = oracle.gemm(fmt, qa_o, sa_o, qw_o, sw_o, want_acc=True)
+        _, _, yi = gpu_linear(fmt, x, wq, ws, N, c, out_type=q.QLIN_OUT_I32_ACC, ldx=ldx)
+        assert np.array_equal(yi.cpu().numpy(), acc), "int32 accumulators differ"
+
+
+LAYER_CFGS = {
+    "fused": cfg(1, 1, 16, 32, 4, 4, fuse=1),
+    "fused_std": cfg(0, 1, 16, 64, 8, 4, fuse=1),
+    "fused_split": cfg(1, 4, 16, 32, 4, 2, fuse=1),
+    "fused_split_std": cfg(0, 3, 16, 16, 8, 8, fuse=1),
+    "fused_nr4": cfg(1, 2, 16, 64, 1, 1, fuse=1),
+    "unfused": cfg(1, 2, 16, 32, 4, 4),
+    "unfused_m32": cfg(0, 2, 32, 64, 4, 2),
+}
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("name", list(LAYER_CFGS))
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_linear_fused_and_unfused(fmt, name, M):
+    N, K = 512, 1536
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 50 + M)
+    check_layer(fmt, M, N, K, x, w, LAYER_CFGS[name])
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_linear_fused_packed_phases_and_stride(fmt):
+    """Fused quantization with packed reduction, with LDS phases (16 rows x
+    8192 codes exceed one stage) and a row stride larger than K."""
+    M, N, K = 16, 256, 8192
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 61)
+    red = 1 if fmt != wl.BLOCK_FP8 else 0
+    check_layer(fmt, M, N, K, x, w, cfg(1, 1, 16, 32, 4, 2, fuse=1), ldx=K + 32)
+    check_layer(fmt, M, N, K, x, w, cfg(1, 2, 16, 64, 4, 4, reduce=red, fuse=1), ldx=K + 32)
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
+def test_linear_fused_ragged_k(fmt):
+    M, N, K = 5, 256, 1040
+    x = wl.random_bf16((M, K), 70)
+    w = wl.random_weights(N, K, 71)
+    for c in (cfg(1, 1, 16, 32, 4, 4, fuse=1), cfg(1, 3, 16, 32, 2, 2, reduce=1, fuse=1)):
+        check_layer(fmt, M, N, K, x, w, c)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_linear_selected_schedule(fmt):
+    for M in (1, 4, 24):
+        N, K = 512, 2048
+        x = wl.activations(fmt, N, K, M)
+        w = wl.random_weights(N, K, 80 + M)
+        check_layer(fmt, M, N, K, x, w, None)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
@@ -190,10 +274,11 @@ def test_e4m3_conversion_exhaustive_at_unit_scale():
     assert np.array_equal(as_u8(xq), qa_o)
 
 
-@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
-def test_splitk_workspace_left_zero_and_reusable(fmt):
+@pytest.mark.parametrize("fmt,red", [(wl.FP8_DYNAMIC, 0), (wl.W8A8_INT8, 0), (wl.BLOCK_FP8, 0),
+                                     (wl.FP8_DYNAMIC, 1), (wl.W8A8_INT8, 1)])
+def test_splitk_workspace_left_zero_and_reusable(fmt, red):
     M, N, K = 5, 512, 2048
-    c = cfg(1, 8, 16, 32, 4, 2)
+    c = cfg(1, 8, 16, 32, 4, 2, reduce=red)
     x = wl.activations(fmt, N, K, M)
     w = wl.random_weights(N, K, 12)
     wq, ws = gpu_quant_weight(fmt, w)
@@ -207,6 +292,26 @@ def test_splitk_workspace_left_zero_and_reusable(fmt):
         assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("fmt,red", [(wl.FP8_DYNAMIC, 0), (wl.W8A8_INT8, 0), (wl.BLOCK_FP8, 0),
+                                     (wl.FP8_DYNAMIC, 1), (wl.W8A8_INT8, 1)])
+def test_splitk_is_deterministic(fmt, red):
+    """Slices are added in partition order and packed partials as exact
+    integers, so repeated runs give identical bits whatever order the
+    partitions finish in."""
+    M, N, K = 24, 1024, 4096
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 14)
+    wq, ws = gpu_quant_weight(fmt, w)
+    xq, xs = gpu_quant_act(fmt, x)
+    c = cfg(1, 16, 32, 32, 4, 4, reduce=red)
+    work = workspace_for(fmt, M, N, K, c)
+    first = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, q.QLIN_OUT_F32_ACC, work)
+    for _ in range(10):
+        again = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, q.QLIN_OUT_F32_ACC, work)
+        assert torch.equal(first, again)
+    assert int(work.count_nonzero()) == 0
+
+
 def test_int8_splitk_deterministic_accumulators():
     M, N, K = 32, 1024, 4096
     fmt = wl.W8A8_INT8
@@ -214,9 +319,11 @@ def test_int8_splitk_deterministic_accumulators():
     w = wl.random_weights(N, K, 13)
     wq, ws = gpu_quant_weight(fmt, w)
     xq, xs = gpu_quant_act(fmt, x)
-    c = cfg(1, 16, 32, 32, 4, 4)
-    work = workspace_for(fmt, M, N, K, c)
-    first = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, q.QLIN_OUT_I32_ACC, work)
+    nbytes = max(q.qlin_workspace_bytes(fmt, M, N, K, cfg(1, 16, 32, 32, 4, 4, reduce=r)) for r in (0, 1))
+    work = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    first = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, cfg(1, 16, 32, 32, 4, 4), q.QLIN_OUT_I32_ACC, work)
+    # one workspace serves both reductions and any shape that fits it
+    c = cfg(1, 16, 32, 32, 4, 4, reduce=1)
     for _ in range(20):
         again = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, q.QLIN_OUT_I32_ACC, work)
         assert torch.equal(first, again)
