@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--detail", default=None, help="write per-shape GEMM timings (JSON) here")
     ap.add_argument("--gemm-only-steps", type=int, default=None,
                     help="replay only the GEMM graphs this many times (for profiling)")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many bytes three "
+                         "times (reference dispatches for the memory-traffic counters)")
     return ap.parse_args()
 
 
@@ -77,6 +80,21 @@ class Linear:
         import skinny_bit_gemm_amd as q
         q.qlin_gemm(self.fmt, self.M, self.N, self.K, self.xq, self.xs, self.wq if wq is None else wq,
                     self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work, stream=stream)
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernels or the table changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = lambda p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha("skinny_bit_gemm_amd/csrc/qlin_kernels.hip") or \
+            rec.get("table_sha256") != sha("skinny_bit_gemm_amd/tables/gfx950.tbl"):
+        return None
+    return rec
 
 
 def capture(stream, fn):
@@ -148,6 +166,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q.lib()
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # quantized weights (GPU quantizer, offline and untimed), then rotating copies
     base = {}
@@ -282,6 +307,12 @@ def main():
             "bytes_per_launch": round(gemm_bytes / n_gemm),
         },
     }
+    tr = measured_traffic(args.workload)
+    if tr is not None:
+        out["roofline"]["traffic"] = tr["per_launch_traffic_bytes"]
+        out["roofline"]["traffic_unit"] = "B per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        out["roofline"]["traffic_vs_algorithmic"] = round(
+            tr["per_launch_traffic_bytes"] / tr["per_launch_algorithmic_bytes"], 3)
     if detail:
         with open(args.detail, "w") as f:
             json.dump(detail, f, indent=1)
