@@ -22,6 +22,8 @@ STATUS = {
     0: "QLIN_OK", 1: "QLIN_ERR_INVALID_ARG", 2: "QLIN_ERR_ALIGNMENT", 3: "QLIN_ERR_SHAPE",
     4: "QLIN_ERR_WORKSPACE", 5: "QLIN_ERR_NO_CONFIG", 6: "QLIN_ERR_TABLE", 7: "QLIN_ERR_HIP",
 }
+(QLIN_OK, QLIN_ERR_INVALID_ARG, QLIN_ERR_ALIGNMENT, QLIN_ERR_SHAPE, QLIN_ERR_WORKSPACE,
+ QLIN_ERR_NO_CONFIG, QLIN_ERR_TABLE, QLIN_ERR_HIP) = range(8)
 
 # every symbol include/qlin.h declares
 EXPORTS = (

@@ -19,7 +19,8 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
-SOURCES = ["qlin_kernels.hip", "qlin_api.cpp", "qlin_table.cpp"]
+SOURCES = ["qlin_gemm_fp8.hip", "qlin_gemm_i8.hip", "qlin_gemm_block.hip", "qlin_kernels.hip",
+           "qlin_api.cpp", "qlin_table.cpp"]
 
 
 def _hipcc() -> str:
@@ -29,7 +30,7 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, jobs: int = 3) -> str:
+def build(verbose: bool = False, jobs: int = 6) -> str:
     """Compile every source and link libqlin.so; returns its path."""
     hipcc = _hipcc()
     os.makedirs(OUT_DIR, exist_ok=True)

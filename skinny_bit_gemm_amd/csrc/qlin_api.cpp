@@ -75,7 +75,6 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     const int nw = c.waves / c.k_waves;
     if (c.tile_n < 16 || c.tile_n > 256 || c.tile_n % (16 * nw) != 0) return QLIN_ERR_INVALID_ARG;
     const int nr = c.tile_n / (16 * nw);
-    if (!gemm_variant_exists(fmt, c.tile_m, nr, fuse)) return QLIN_ERR_INVALID_ARG;
     const int mt = c.tile_m / 16;
     p->tile_m = c.tile_m;
     p->tile_n = c.tile_n;
@@ -94,6 +93,22 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     int pb = kLdsBudget / per_block;
     if (pb > p->kb_per_split) pb = p->kb_per_split;
     p->phase_blocks = pb;
+    // In-kernel quantization: one phase (the workgroup's K range fits the
+    // LDS), and the tile's activation chunks of 8 values, spread over the
+    // workgroup's threads, fit in 8 register chunks per thread: whole rows
+    // for the per-token formats (the amax is over all of K; rows are padded
+    // to a multiple of 64 chunks), the range for the block format.
+    int xc = 0;
+    if (fuse) {
+        if (pb < p->kb_per_split) return QLIN_ERR_INVALID_ARG;
+        const int chunks = fmt == QLIN_BLOCK_FP8 ? p->kb_per_split * 16 : (K / 8 + 63) / 64 * 64;
+        const int threads = 64 * c.waves;
+        const int need = (rows * chunks + threads - 1) / threads;
+        xc = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
+        if (xc == 0) return QLIN_ERR_INVALID_ARG;
+    }
+    p->xc = xc;
+    if (!gemm_variant_exists(fmt, c.tile_m, nr, xc)) return QLIN_ERR_INVALID_ARG;
     size_t lds = (size_t)pb * per_block;
     const size_t red = (size_t)(c.k_waves - 1) * nw * nr * mt * 64 * 16;
     if (red > lds) lds = red;
@@ -241,7 +256,7 @@ qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, cons
     GemmLaunch g = launch_args(p, M, N, K, wq, w_scales, y, out_type, workspace);
     g.xq = static_cast<const uint8_t *>(xq);
     g.xs = x_scales;
-    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, false, g, p.lds_bytes,
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, 0, g, p.lds_bytes,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -258,6 +273,13 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
     if (ldx < K || ldx % 8 != 0) return QLIN_ERR_ALIGNMENT;
     if (!aligned16(x) || !aligned16(xq)) return QLIN_ERR_ALIGNMENT;
     if (M == 0) return QLIN_OK;
+    // the in-kernel quantization addresses the tile's rows of x with 32-bit
+    // byte offsets; a very wide row stride takes the two-kernel path
+    if (p.fuse && ((int64_t)((M < c.tile_m ? M : c.tile_m) - 1) * ldx + K) * 2 >= ((int64_t)1 << 31)) {
+        c.fuse_quant = 0;
+        st = make_plan(fmt, M, N, K, c, true, &p);
+        if (st != QLIN_OK) return st;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     GemmLaunch g = launch_args(p, M, N, K, wq, w_scales, y, out_type, workspace);
     if (p.fuse) {
@@ -271,7 +293,7 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
         g.xq = static_cast<const uint8_t *>(xq);
         g.xs = x_scales;
     }
-    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, p.fuse, g, p.lds_bytes, s));
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, p.xc, g, p.lds_bytes, s));
 }
 
 struct qlin_graph_s {
@@ -291,11 +313,11 @@ qlin_status qlin_graph_end(void *stream, qlin_graph *graph) {
     if (st != QLIN_OK) return st;
     hipGraphExec_t exec = nullptr;
     st = hip_status(hipGraphInstantiate(&exec, g, nullptr, nullptr, 0));
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);   // the executable graph keeps what it needs
     if (st != QLIN_OK) return st;
     qlin_graph h = new (std::nothrow) qlin_graph_s;
     if (!h) {
-        hipGraphExecDestroy(exec);
+        (void)hipGraphExecDestroy(exec);
         return QLIN_ERR_INVALID_ARG;
     }
     h->exec = exec;

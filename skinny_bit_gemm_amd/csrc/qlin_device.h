@@ -1,0 +1,110 @@
+// qlin_device.h -- device-side helpers shared by the quantization and GEMM
+// kernels: operand vector types, the fp32 -> e4m3 / int8 code conversions,
+// bf16 unpacking and rounding, and wave reductions.
+//
+// Quantization rules: "Building a High-Performance and Portable vLLM Linear
+// Backend with Helion", section "Scope" (symmetric scales: amax over a token
+// row, a 1x128 group, a channel or a 128x128 block, divided by the format's
+// largest code).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "qlin_internal.h"
+
+namespace qlin {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+enum { FMT_FP8 = QLIN_FP8_DYNAMIC, FMT_I8 = QLIN_W8A8_INT8, FMT_BLOCK = QLIN_BLOCK_FP8 };
+
+// ------------------------------------------------------------ conversions
+
+// fp32 -> fp8 E4M3FN code.  Magnitudes at or above 448 saturate to 448
+// (0x7E); normal results round the 23-bit mantissa to 3 bits, nearest with
+// ties to even, carrying into the exponent; below 2^-6 the value is a whole
+// multiple of 2^-9, so |v| * 512 (exact) is rounded to an integer 0..8 (8 is
+// the code of 2^-6).  The sign bit is copied, so -0 and tiny negatives give
+// 0x80.  Inputs are finite.  All three cases are computed and one selected,
+// so a wave converts without diverging.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);   // rebias 127 -> 7
+    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    const uint32_t mag = a >= 0x43E00000u ? 0x7Eu : (a >= 0x3C800000u ? normal : sub);  // 448, 2^-6
+    return sign | mag;
+}
+
+// code of one value given its row/group scale (scale 0: the run was zero,
+// and so is every code; the quotient is computed anyway and discarded)
+template <int FMT>
+__device__ __forceinline__ uint32_t quant_code(float x, float s) {
+    const float t = x / s;   // IEEE division, correctly rounded
+    uint32_t code;
+    if constexpr (FMT == FMT_I8) {
+        float r = __builtin_rintf(t);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        code = (uint32_t)(int32_t)r & 0xFFu;
+    } else {
+        code = e4m3_code(t);
+    }
+    return s == 0.0f ? 0u : code;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, nearest with ties to even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int FMT>
+__device__ __forceinline__ float qmax_of() { return FMT == FMT_I8 ? 127.0f : 448.0f; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// --------------------------------------------------- activation quantization
+
+// bf16 x 8 (one 16-byte chunk) -> max |value|.  For finite bf16 values the
+// magnitude bits (sign cleared) order like the magnitudes, so the maximum is
+// taken on the integer halves and converted once; the values themselves are
+// not unpacked here.
+__device__ __forceinline__ uint32_t absmax2_bits(uint32_t w) {
+    return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+__device__ __forceinline__ float absmax8(uint4 v) {
+    const uint32_t m = max(max(absmax2_bits(v.x), absmax2_bits(v.y)),
+                           max(absmax2_bits(v.z), absmax2_bits(v.w)));
+    return __uint_as_float(m << 16);
+}
+
+// bf16 x 8 -> 8 codes packed little-endian into two words.  The values are
+// converted one after another: each IEEE division holds a scalar register
+// pair for its scaling flag, and left to interleave many of them the
+// scheduler runs out of scalar registers (a wave issues one vector
+// instruction at a time either way).
+template <int FMT>
+__device__ __forceinline__ uint2 quant8(uint4 v, float s) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t word = w[j >> 1];
+        const float x = (j & 1) ? bf16_hi(word) : bf16_lo(word);
+        out[j >> 2] |= quant_code<FMT>(x, s) << (8 * (j & 3));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return make_uint2(out[0], out[1]);
+}
+
+}  // namespace qlin

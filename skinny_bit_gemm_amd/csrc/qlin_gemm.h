@@ -1,0 +1,698 @@
+// qlin_gemm.h -- the skinny quantized GEMM kernel for gfx950 (CDNA4), with
+// its Standard / Split-K / Swap-AB schedules and the optional in-kernel
+// activation quantization.  Included by one source file per format, each of
+// which instantiates the variants it dispatches to.
+//
+// Product: "Building a High-Performance and Portable vLLM Linear Backend
+// with Helion", section "Scope" (FP8_Dynamic, W8A8_INT8, Block_FP8 scale
+// granularities) and section "Kernel Implementation" (one contraction with
+// a float32 accumulator, split_k / swap_ab as schedule choices, Split-K
+// partials added into a zeroed output).
+//
+// Data layout (all row-major): activations x bf16 [M][ldx], codes xq [M][K],
+// weights wq [N][K] (K contiguous, as a torch Linear weight), output y [M][N].
+#pragma once
+
+#include "qlin_device.h"
+
+namespace qlin {
+
+// ---------------------------------------------------------------------------
+//
+// Work decomposition.  A workgroup owns a tile of up to TM = 16*MT tokens by
+// TN = 16*NR*nw output channels and a range of 128-wide K blocks (all of K,
+// or one Split-K partition).  Its waves form an nw x kw grid: a wave owns NR
+// sub-tiles of 16 channels and every kw-th K block of the range, so the kw
+// waves of a column stream neighbouring K blocks of the same weight rows at
+// the same time; their partial sums are added through LDS at the end.
+//
+// Operand fragments.  For one 128-wide K block a lane l (row r = l % 16,
+// quarter q = l / 16) holds 32 consecutive bytes k = 32q .. 32q+31 of its
+// row, for the weight row (channel n0 + r) and for the activation row
+// (token m0 + r).  Both matrix-core operands use the same lane -> (row, k)
+// assignment, so whatever order the hardware sums the k slots in, every
+// weight byte meets the activation byte of the same k.  fp8 uses one
+// 16x16x128 MFMA per block (32 bytes per lane); int8 uses two 16x16x64 MFMAs
+// (bytes 0..15, then 16..31 of each lane's 32).
+//
+// Weight stream.  Each weight lane load covers 32 contiguous bytes; the 4
+// lanes of a row cover the row's whole 128-byte block, so a wave-wide load
+// reads 16 full 128-byte lines.  A wave keeps PF blocks of loads in flight
+// in PF register slots, consumed and refilled in batches.
+//
+// Activations.  The workgroup's token rows for its K range are staged once
+// in LDS, only the rows that exist (R = min(TM, M - m0)), laid out as
+// [K block][half][quarter][row][16 bytes]: the 16 lanes of a quarter read 16
+// consecutive 16-byte chunks, so the two ds_read_b128 per block are free of
+// bank conflicts.  Lanes whose row is past R use zeros.  When R x (K range)
+// does not fit the LDS budget the range is processed in phases.
+//
+// Order of the memory requests.  The vector memory counter a wave waits on
+// counts requests in issue order, so a wait for one load is a wait for every
+// older one.  Each phase therefore first requests its activations (codes,
+// or bf16 values to quantize), then the first PF weight blocks, then the
+// epilogue's scales; the activations arrive first (they are few and
+// L2-resident) and are staged in LDS while the weights are still in
+// flight.  Every weight slot is requested on every path (a slot past the
+// wave's last block uses an out-of-range offset, which returns zeros without
+// touching memory), so the compiler's waits count exactly.
+//
+// Standard: A = activations (tokens are the MFMA rows), B = weights.  The
+// 16x16 result lane l holds column l % 16 = channel and rows 4(l/16)+i =
+// tokens.  Swap-AB: A = weights, B = activations, so the result is the
+// transpose: lane l holds token l % 16 and channels 4(l/16)+i, which makes
+// the output stores 4 channels wide and needs one activation scale per lane.
+//
+// In-kernel quantization (XC > 0, per-token formats and the block format):
+// each wave owns whole token rows (rows w, w + waves, ...) and holds up to
+// XC 8-value chunks of them per lane in registers, so the activations are
+// read once: per-token formats take the row's amax over all of K by a wave
+// reduction (the rows are small and shared by every workgroup, so they come
+// from L2), the block format the 1x128 group amax over the 16 lanes that
+// hold a group.  The codes of the workgroup's K range are written to the
+// LDS staging layout directly.
+
+template <int FMT>
+struct AccT;
+template <>
+struct AccT<FMT_I8> {
+    typedef v4i type;
+    typedef int scalar;
+};
+template <>
+struct AccT<FMT_FP8> {
+    typedef v4f type;
+    typedef float scalar;
+};
+template <>
+struct AccT<FMT_BLOCK> {
+    typedef v4f type;
+    typedef float scalar;
+};
+
+__device__ __forceinline__ v8i join(uint4 lo, uint4 hi) {
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+__device__ __forceinline__ v4i lo4(v8i v) { return v4i{v[0], v[1], v[2], v[3]}; }
+__device__ __forceinline__ v4i hi4(v8i v) { return v4i{v[4], v[5], v[6], v[7]}; }
+
+// acc (+)= A . B for one 128-wide K block
+template <int FMT>
+__device__ __forceinline__ typename AccT<FMT>::type block_mma(v8i a, v8i b,
+                                                              typename AccT<FMT>::type c) {
+    if constexpr (FMT == FMT_I8) {
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(lo4(a), lo4(b), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi4(a), hi4(b), c, 0, 0, 0);
+        return c;
+    } else {
+        // operand formats 0/0 = fp8 E4M3 for A and B; zero scale operands
+        // select the unscaled instruction
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint4 select4(bool keep, uint4 v) {
+    return keep ? v : make_uint4(0, 0, 0, 0);
+}
+
+// Buffer resources: base address and size in bytes; the hardware checks
+// every access against the size, and an offset at or past it returns zeros
+// and makes no memory access.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kBufferFormat = 0x00020000;   // descriptor word 3 for gfx9-family targets
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFormat);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 32 bytes of the lane's weight row in K block kb (lane_off = row * K + 32 *
+// quarter, in a resource that covers one 16-row sub-tile; k = the lane's
+// first K index).  The block's offset is a scalar operand, so a slot costs
+// no address registers.  A 16-byte half at or past K (in a partial last
+// block), or a dead slot, uses an out-of-range lane offset, so every lane
+// issues the same two loads per block and nothing has to be masked after
+// the data arrives.
+__device__ __forceinline__ v8i load_w(__amdgpu_buffer_rsrc_t rs, uint32_t lane_off, int kb, int k,
+                                      int K, bool live) {
+    const int boff = __builtin_amdgcn_readfirstlane(kb * kGroup);
+    const uint32_t lo_off = live && k < K ? lane_off : kOutOfRange;
+    const uint32_t hi_off = live && k + 16 < K ? lane_off : kOutOfRange;
+    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(rs, lo_off, boff, 0);
+    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rs, hi_off, boff + 16, 0);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Orders this thread's earlier global atomics before what follows: wait for
+// every outstanding memory operation to be acknowledged.  (Device-scope
+// atomics are coherent across the chip's L2 slices; what the arrival counter
+// needs is only that a partition's additions are performed before its
+// arrival is counted.  A device-scope release fence would also write back
+// the whole L2, which costs far more than the kernel.)
+__device__ __forceinline__ void wait_memory_idle() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// byte offset in the LDS staging layout [block][half][quarter][row][16B] of
+// 8-byte chunk cl (0, 1, ... along the K range) of row `row` (R rows)
+__device__ __forceinline__ int stage_offset8(int cl, int row, int R) {
+    const int b = cl >> 4, cc = cl & 15, u = cc >> 1;
+    return (((b * 2 + (u & 1)) * 4 + (u >> 1)) * R + row) * 16 + (cc & 1) * 8;
+}
+
+// activation 16-byte units staged per thread straight from registers (the
+// rest, for very large tiles, in a loop afterwards)
+constexpr int kStageRegs = 4;
+
+template <int FMT, bool SWAP, int MT, int NR, int PF, int XC>
+__global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
+    typedef typename AccT<FMT>::type acc_t;
+    typedef typename AccT<FMT>::scalar acc_s;
+    constexpr bool FUSE = XC > 0;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int s_last;
+    __shared__ float s_rowscale[16 * MT];
+    __shared__ float s_seg[FUSE ? XC * kMaxWaves : 1];   // per-token amax of 64-chunk segments
+
+    const int lane = threadIdx.x & 63;
+    // wave-level values are made explicitly uniform (scalar registers), so
+    // the block loop below branches on scalars
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nthreads = blockDim.x;
+    const int nwaves = nthreads >> 6;
+    const int nw = wave % g.nw, kw = wave / g.nw;
+    const int TN = 16 * NR * g.nw;
+    const int n_tile0 = blockIdx.x * TN;
+    const int m0 = blockIdx.y * 16 * MT;
+    const int kb_begin = blockIdx.z * g.kb_per_split;
+    const int kb_end = min(g.nkb, kb_begin + g.kb_per_split);
+    const int M = g.M, N = g.N, K = g.K;
+    const int r16 = lane & 15, quarter = lane >> 4;
+    const int G = (K + kGroup - 1) / kGroup;
+    const int R = min(16 * MT, M - m0);   // token rows that exist in this tile
+    // fused path: the first column of workgroups also stores the codes and
+    // scales it produces (every workgroup of a row of tiles produces the same)
+    const bool writer = FUSE && blockIdx.x == 0;
+
+    int nsub[NR];
+    __amdgpu_buffer_rsrc_t wrs[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        nsub[r] = n_tile0 + (nw * NR + r) * 16;
+        // sub-tiles past N get an empty resource: their loads return zeros
+        const int base = min(nsub[r], N - 16);
+        wrs[r] = buffer_rsrc(g.wq + (int64_t)base * K, nsub[r] < N ? 16u * K : 0u);
+    }
+    const uint32_t lane_off = (uint32_t)(r16 * K + quarter * 32);
+    // the lane's activation fragment in a staged block: [half 0][quarter][row]
+    // (rows past R read an existing row, and their data is replaced by zeros)
+    int lds_lo[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) lds_lo[mt] = (quarter * R + (mt * 16 + r16 < R ? mt * 16 + r16 : 0)) * 16;
+
+    acc_t acc[NR][MT];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = acc_t{0, 0, 0, 0};
+
+    // Per-channel formats: the epilogue's channel (and, unfused, token)
+    // scales, requested after the first weight blocks so that their latency
+    // hides behind the weight stream.  Swap-AB lanes need one token scale and
+    // 4 channel scales per sub-tile, Standard lanes 4 token scales and one
+    // channel scale.
+    float pre_sa[MT][SWAP ? 1 : 4], pre_sw[NR][SWAP ? 4 : 1];
+    auto token_of = [&](int mt, int i) { return SWAP ? m0 + mt * 16 + r16 : m0 + mt * 16 + 4 * quarter + i; };
+    // (buffer loads: 32-bit offsets, and positions past N or M read zeros)
+    auto prefetch_scales = [&]() {
+        if constexpr (FMT != FMT_BLOCK) {
+            const __amdgpu_buffer_rsrc_t wsr = buffer_rsrc(g.wsc, (uint32_t)N * 4);
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int i = 0; i < (SWAP ? 4 : 1); ++i) {
+                    const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
+                    pre_sw[r][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wsr, n * 4, 0, 0));
+                }
+            if constexpr (!FUSE) {
+                const __amdgpu_buffer_rsrc_t xsr = buffer_rsrc(g.xs + m0, (uint32_t)R * 4);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < (SWAP ? 1 : 4); ++i)
+                        pre_sa[mt][i] = __uint_as_float(
+                            __builtin_amdgcn_raw_buffer_load_b32(xsr, (token_of(mt, i) - m0) * 4, 0, 0));
+            }
+        }
+    };
+
+    // request K block kb into a register slot (the block format also fetches
+    // each sub-tile's 128x128 weight-block scale); a dead slot (live false)
+    // is requested with out-of-range offsets
+    auto issue = [&](v8i(&slot)[NR], float(&sws)[NR], int kb, bool live) {
+        const int k = kb * kGroup;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            slot[r] = load_w(wrs[r], lane_off, kb, k + quarter * 32, K, live);
+            if constexpr (FMT == FMT_BLOCK)
+                sws[r] = g.wsc[(int64_t)(min(nsub[r], N - 1) / kGroup) * G + min(kb, G - 1)];
+        }
+    };
+
+    v8i wbuf[PF][NR];
+    float wsbuf[PF][NR];
+    const int kstep = g.kw;
+
+    for (int pb0 = kb_begin; pb0 < kb_end; pb0 += g.phase_blocks) {
+        const int nblk = min(kb_end - pb0, g.phase_blocks);
+        // this wave's blocks of the phase are kw, kw + kstep, ... (a uniform count)
+        const int nmine = kw < nblk ? (nblk - kw + kstep - 1) / kstep : 0;
+        float *s_scale = reinterpret_cast<float *>(smem + (size_t)g.phase_blocks * kGroup * R);
+
+        // ---- 1. activation requests
+        // fused: the tile's R rows x cn chunk positions of 8 values (per-token
+        // formats: all of K, for the amax, padded to a multiple of 64; block
+        // format: the K range) in a flat order, chunk slots i of thread t =
+        // t + i * nthreads (the fused path has a single phase: its range
+        // fits the LDS)
+        const int nchunk = K >> 3;
+        const int c_lo = FMT == FMT_BLOCK ? kb_begin * 16 : 0;
+        const int cn = FMT == FMT_BLOCK ? (kb_end - kb_begin) * 16 : (nchunk + 63) & ~63;
+        const int row0 = threadIdx.x / cn, c0 = threadIdx.x - row0 * cn;
+        const int t_rows = nthreads / cn, t_chunks = nthreads - t_rows * cn;
+        auto next_slot = [&](int &row, int &c) {
+            c += t_chunks;
+            row += t_rows;
+            if (c >= cn) { c -= cn; ++row; }
+        };
+        uint4 xr[FUSE ? XC : 1];
+        // unfused: the first kStageRegs 16-byte units of codes per thread
+        // (and, block format, one activation scale)
+        const int items = R * nblk * 8;
+        uint4 sv[FUSE ? 1 : kStageRegs];
+        int spos[FUSE ? 1 : kStageRegs];   // LDS byte position of each, or -1
+        float sx = 0.0f;
+        if constexpr (FUSE) {
+            const __amdgpu_buffer_rsrc_t xrs =
+                buffer_rsrc(g.x + (int64_t)m0 * g.ldx, (uint32_t)(((R - 1) * g.ldx + K) * 2));
+            int row = row0, c = c0;
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+                const bool ok = row < R && c_lo + c < nchunk;
+                xr[i] = load16(xrs, ok ? (uint32_t)((row * g.ldx + (c_lo + c) * 8) * 2) : kOutOfRange);
+                next_slot(row, c);
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(g.xq + (int64_t)m0 * K, (uint32_t)(R * K));
+#pragma unroll
+            for (int s = 0; s < kStageRegs; ++s) {
+                const int it = threadIdx.x + s * nthreads;
+                const int c = it & 7, rest = it >> 3;
+                const int b = rest % nblk, row = rest / nblk;
+                const int k = (pb0 + b) * kGroup + c * 16;
+                sv[s] = load16(qrs, it < items && k < K ? (uint32_t)(row * K + k) : kOutOfRange);
+                spos[s] = it < items ? (((b * 2 + (c & 1)) * 4 + (c >> 1)) * R + row) * 16 : -1;
+            }
+            if constexpr (FMT == FMT_BLOCK) {
+                const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(g.xs + (int64_t)m0 * G, (uint32_t)(R * G * 4));
+                const int it = threadIdx.x;
+                const int row = it % R, b = it / R;
+                const uint32_t off = it < nblk * R ? (uint32_t)((row * G + pb0 + b) * 4) : kOutOfRange;
+                sx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+            }
+        }
+
+        // ---- 2. the epilogue's scales, then the first batch of weight blocks
+        // (the weight loads are always the youngest requests in flight; the
+        // scheduling barriers keep the compiler from sinking the earlier
+        // requests below them)
+        prefetch_scales();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(wbuf[p], wsbuf[p], pb0 + kw + p * kstep, p < nmine);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- 3. activations into LDS
+        if (pb0 != kb_begin) __syncthreads();   // the previous phase's readers are done
+        if constexpr (FUSE) {
+            const int kc0 = kb_begin * 16, kc1 = kb_end * 16;   // chunks staged (absolute)
+            auto stage8 = [&](int row, int c, uint2 codes) {   // c absolute
+                *reinterpret_cast<uint2 *>(smem + stage_offset8(c - kc0, row, R)) = codes;
+                if (writer && c < nchunk)
+                    *reinterpret_cast<uint2 *>(g.xq_out + (int64_t)(m0 + row) * K + c * 8) = codes;
+            };
+            if constexpr (FMT == FMT_BLOCK) {
+                // one 1x128 group = 16 chunks = 16 neighbouring lanes (cn and
+                // nthreads are multiples of 16)
+                int row = row0, c = c0;
+#pragma unroll
+                for (int i = 0; i < XC; ++i) {
+                    float amax = absmax8(xr[i]);
+#pragma unroll
+                    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+                    const float sc = amax == 0.0f ? 0.0f : amax / 448.0f;
+                    if (row < R) {
+                        stage8(row, c_lo + c, quant8<FMT>(xr[i], sc));
+                        if ((c & 15) == 0) {
+                            s_scale[(c >> 4) * R + row] = sc;
+                            if (writer) g.xs_out[(int64_t)(m0 + row) * G + kb_begin + (c >> 4)] = sc;
+                        }
+                    }
+                    next_slot(row, c);
+                }
+            } else {
+                // per-token amax: cn and nthreads are multiples of 64, so the
+                // 64 chunks of one wave and slot lie in one row; their
+                // maximum is segment (t + i * nthreads) / 64 of the flat
+                // order, and a row's amax is the maximum of its cn / 64
+                // segments.  Positions past K hold zeros; those in the last
+                // (partial) K block are staged as zero codes.
+                const int segs = cn >> 6;
+                {
+                    int row = row0, c = c0;
+#pragma unroll
+                    for (int i = 0; i < XC; ++i) {
+                        const float a = wave_max(absmax8(xr[i]));
+                        if (row < R && lane == 0) s_seg[(row * cn + c) >> 6] = a;
+                        next_slot(row, c);
+                    }
+                }
+                __syncthreads();
+                int row = row0, c = c0;
+#pragma unroll
+                for (int i = 0; i < XC; ++i) {
+                    if (row < R) {
+                        float amax = 0.0f;
+                        for (int sg = 0; sg < segs; ++sg) amax = fmaxf(amax, s_seg[row * segs + sg]);
+                        const float sc = amax == 0.0f ? 0.0f : amax / qmax_of<FMT>();
+                        if (c == 0) {
+                            s_rowscale[row] = sc;
+                            if (writer && blockIdx.z == 0) g.xs_out[m0 + row] = sc;
+                        }
+                        if (c >= kc0 && c < kc1) stage8(row, c, quant8<FMT>(xr[i], sc));
+                    }
+                    next_slot(row, c);
+                }
+            }
+        } else {
+            auto put = [&](int it, uint4 v) {
+                const int c = it & 7, rest = it >> 3;
+                const int b = rest % nblk, row = rest / nblk;
+                *reinterpret_cast<uint4 *>(smem + (((b * 2 + (c & 1)) * 4 + (c >> 1)) * R + row) * 16) = v;
+            };
+#pragma unroll
+            for (int s = 0; s < kStageRegs; ++s)
+                if (spos[s] >= 0) *reinterpret_cast<uint4 *>(smem + spos[s]) = sv[s];
+            for (int it = threadIdx.x + kStageRegs * nthreads; it < items; it += nthreads) {
+                const int c = it & 7, rest = it >> 3;
+                const int b = rest % nblk, row = rest / nblk;
+                const int k = (pb0 + b) * kGroup + c * 16;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (k < K) v = *reinterpret_cast<const uint4 *>(g.xq + (int64_t)(m0 + row) * K + k);
+                put(it, v);
+            }
+            if constexpr (FMT == FMT_BLOCK) {
+                if ((int)threadIdx.x < nblk * R) s_scale[threadIdx.x] = sx;   // [block][row]
+                for (int it = threadIdx.x + nthreads; it < nblk * R; it += nthreads) {
+                    const int row = it % R, b = it / R;
+                    s_scale[it] = g.xs[(int64_t)(m0 + row) * G + pb0 + b];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- 4. the weight stream
+        // one block: MFMAs of the weights in slot p against this wave's block
+        // jb of the phase
+        auto compute = [&](int p, int jb) {
+            const int b = kw + jb * kstep;
+            // activation fragments of this block (zeros past row R; the read
+            // address is clamped to an existing row)
+            const int boff = __builtin_amdgcn_readfirstlane(b * 8 * R * 16);   // uniform
+            v8i xf[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bool live = mt * 16 + r16 < R;
+                const uint4 lo = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + boff);
+                const uint4 hi = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + 4 * R * 16 + boff);
+                xf[mt] = join(select4(live, lo), select4(live, hi));
+            }
+            if constexpr (FMT == FMT_BLOCK) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const float swv = wsbuf[p][r];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const v4f t = SWAP ? block_mma<FMT>(wbuf[p][r], xf[mt], v4f{0, 0, 0, 0})
+                                           : block_mma<FMT>(xf[mt], wbuf[p][r], v4f{0, 0, 0, 0});
+                        const float *sc = s_scale + b * R;
+                        if (SWAP) {
+                            const int row = mt * 16 + r16;
+                            const float c = (row < R ? sc[row] : 0.0f) * swv;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[r][mt][i] += t[i] * c;
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int row = mt * 16 + 4 * quarter + i;
+                                acc[r][mt][i] += t[i] * ((row < R ? sc[row] : 0.0f) * swv);
+                            }
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[r][mt] = SWAP ? block_mma<FMT>(wbuf[p][r], xf[mt], acc[r][mt])
+                                          : block_mma<FMT>(xf[mt], wbuf[p][r], acc[r][mt]);
+            }
+        };
+
+        // Batches of PF blocks: compute a batch, then request the next one
+        // into the same slots (every slot on every pass, dead ones out of
+        // range).  One loop body for every batch, so the slots live in the
+        // same registers on every path.  Per-block work is a few MFMAs
+        // against the memory latency; the other waves of the compute unit
+        // keep the memory system busy while one computes.
+        for (int j = 0;; j += PF) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p)
+                if (j + p < nmine) compute(p, j + p);
+            if (j + PF >= nmine) break;
+#pragma unroll
+            for (int p = 0; p < PF; ++p)
+                issue(wbuf[p], wsbuf[p], pb0 + kw + (j + PF + p) * kstep, j + PF + p < nmine);
+        }
+    }
+
+    if constexpr (FUSE && FMT != FMT_BLOCK) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < (SWAP ? 1 : 4); ++i) {
+                const int row = token_of(mt, i) - m0;
+                pre_sa[mt][i] = row < R ? s_rowscale[row] : 0.0f;
+            }
+    }
+
+    // add the partial sums of the kw waves of each column through LDS
+    if (g.kw > 1) {
+        __syncthreads();
+        acc_t *red = reinterpret_cast<acc_t *>(smem);
+        if (kw > 0) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    red[((((kw - 1) * g.nw + nw) * NR + r) * MT + mt) * 64 + lane] = acc[r][mt];
+        }
+        __syncthreads();
+        if (kw == 0) {
+            for (int jw = 1; jw < g.kw; ++jw)
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[r][mt] += red[((((jw - 1) * g.nw + nw) * NR + r) * MT + mt) * 64 + lane];
+        }
+    }
+
+    // output value from a total t (scaled sum for the block format, raw sum
+    // otherwise) for accumulator element (r, mt, i) of this lane
+    auto scaled = [&](float t, int r, int mt, int i) -> float {
+        if constexpr (FMT == FMT_BLOCK) return t;
+        else return (t * pre_sa[mt][SWAP ? 0 : i]) * pre_sw[r][SWAP ? i : 0];
+    };
+    auto store1 = [&](int64_t idx, float o, int raw) {
+        if (g.out_type == QLIN_OUT_I32_ACC) static_cast<int *>(g.y)[idx] = raw;
+        else if (g.out_type == QLIN_OUT_F32_ACC) static_cast<float *>(g.y)[idx] = o;
+        else static_cast<uint16_t *>(g.y)[idx] = (uint16_t)bf16_bits(o);
+    };
+
+    if (g.nsplit == 1) {
+        if (kw != 0) return;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            if (nsub[r] >= N) continue;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (SWAP) {
+                    const int m = m0 + mt * 16 + r16;
+                    const int n = nsub[r] + 4 * quarter;
+                    if (m >= M) continue;
+                    if (g.out_type == QLIN_OUT_I32_ACC) {
+                        *reinterpret_cast<int4 *>(static_cast<int *>(g.y) + (int64_t)m * N + n) =
+                            make_int4((int)acc[r][mt][0], (int)acc[r][mt][1], (int)acc[r][mt][2],
+                                      (int)acc[r][mt][3]);
+                    } else {
+                        float o[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[i] = scaled((float)acc[r][mt][i], r, mt, i);
+                        if (g.out_type == QLIN_OUT_F32_ACC) {
+                            *reinterpret_cast<float4 *>(static_cast<float *>(g.y) + (int64_t)m * N + n) =
+                                make_float4(o[0], o[1], o[2], o[3]);
+                        } else {
+                            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(g.y) + (int64_t)m * N + n) =
+                                make_uint2(bf16_bits(o[0]) | (bf16_bits(o[1]) << 16),
+                                           bf16_bits(o[2]) | (bf16_bits(o[3]) << 16));
+                        }
+                    }
+                } else {
+                    const int n = nsub[r] + r16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = m0 + mt * 16 + 4 * quarter + i;
+                        if (m >= M) continue;
+                        store1((int64_t)m * N + n, scaled((float)acc[r][mt][i], r, mt, i), (int)acc[r][mt][i]);
+                    }
+                }
+            }
+        }
+        return;
+    }
+
+    // Split-K: the partitions' partial sums are combined in one of two ways.
+    //
+    // Packed (exact formats: int8, and fp8 with per-channel scales): one
+    // returning 64-bit atomic per output.  A partition's sum is an integer:
+    // int8 sums are int32, and fp8 products are whole multiples of 2^-18, so
+    // every fp32 partial sum of them is too and p * 2^18 converts exactly.
+    // Each partition adds p + 2^52 to a zeroed element; while |sum| < 2^51
+    // the value returned, old = S + c * 2^52, gives the number c of
+    // partitions that came before and their exact sum S.  The partition that
+    // sees c = nsplit - 1 holds the total, writes the output and zeroes the
+    // element.  One round trip, and the result does not depend on the order.
+    if constexpr (FMT != FMT_BLOCK) {
+        if (g.packed) {
+            if (kw != 0) return;
+            unsigned long long *ws64 = static_cast<unsigned long long *>(g.acc_ws);
+            const unsigned long long kUnit = 1ull << 52, kHalf = 1ull << 51;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (nsub[r] >= N) continue;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = token_of(mt, i);
+                        const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
+                        if (m >= M) continue;
+                        const int64_t idx = (int64_t)m * N + n;
+                        long long v;
+                        if constexpr (FMT == FMT_I8) v = (long long)acc[r][mt][i];
+                        else v = (long long)(acc[r][mt][i] * 262144.0f);
+                        const unsigned long long old = __hip_atomic_fetch_add(
+                            &ws64[idx], (unsigned long long)(v + (long long)kUnit), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+                        const unsigned long long before = (old + kHalf) >> 52;
+                        if (before != (unsigned long long)(g.nsplit - 1)) continue;
+                        const long long total = (long long)(old - before * kUnit) + v;
+                        float t;
+                        if constexpr (FMT == FMT_I8) t = (float)total;
+                        else t = (float)((double)total * (1.0 / 262144.0));
+                        store1(idx, scaled(t, r, mt, i), (int)total);
+                        __hip_atomic_store(&ws64[idx], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+            }
+            return;
+        }
+    }
+
+    // Slices (any format): each partition stores its partial sums into its
+    // own slice of the workspace with device-coherent stores, waits until
+    // they are acknowledged, and counts its arrival for the tile.  The last
+    // partition to arrive adds the slices in partition order (so the result
+    // is deterministic), writes the output, and zeroes the slices and the
+    // counter.
+    acc_s *part = static_cast<acc_s *>(g.acc_ws);
+    const int64_t slice = (int64_t)M * N;
+    if (kw == 0) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            if (nsub[r] >= N) continue;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = token_of(mt, i);
+                    const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
+                    if (m < M)
+                        __hip_atomic_store(&part[blockIdx.z * slice + (int64_t)m * N + n],
+                                           (acc_s)acc[r][mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+        }
+    }
+    wait_memory_idle();
+    __syncthreads();
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&g.counters[tile], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (uint32_t)(g.nsplit - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int tn = min(TN, N - n_tile0);
+    for (int e = threadIdx.x; e < R * tn; e += nthreads) {
+        const int m = m0 + e / tn;
+        const int n = n_tile0 + e % tn;
+        const int64_t idx = (int64_t)m * N + n;
+        acc_s v = 0;
+        for (int z = 0; z < g.nsplit; ++z)
+            v += __hip_atomic_load(&part[z * slice + idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int z = 0; z < g.nsplit; ++z)   // leave the workspace zero
+            __hip_atomic_store(&part[z * slice + idx], (acc_s)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float o;
+        if constexpr (FMT == FMT_BLOCK) o = v;
+        else if constexpr (FUSE) o = ((float)v * s_rowscale[m - m0]) * g.wsc[n];
+        else o = ((float)v * g.xs[m]) * g.wsc[n];
+        store1(idx, o, (int)v);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&g.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// prefetch depth: 8 blocks of 16 weight rows in flight per wave (2 for NR = 4)
+#define QLIN_PF(NR_, XC_) (NR_ >= 4 ? 2 : 8 / NR_)
+
+typedef void (*gemm_fn)(GemmLaunch);
+
+// The kernel for a (format, schedule, tile) choice, or null; defined by the
+// per-format source files.  xc: register chunks of the in-kernel
+// quantization (0 = codes come quantized).
+gemm_fn gemm_pick_fp8(bool swap, int tile_m, int nr, int xc);
+gemm_fn gemm_pick_i8(bool swap, int tile_m, int nr, int xc);
+gemm_fn gemm_pick_block(bool swap, int tile_m, int nr, int xc);
+
+}  // namespace qlin

@@ -1,0 +1,25 @@
+// qlin_gemm_fp8.hip -- the GEMM kernel variants of one format (FMT_FP8), and
+// their dispatch; one source file per format so the variants build in
+// parallel.
+#include "qlin_gemm.h"
+
+namespace qlin {
+
+template <bool SWAP>
+static gemm_fn pick(int tile_m, int nr, int xc) {
+#define QLIN_PICK(MT_, NR_, XC_) \
+    if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_) return gemm_kernel<FMT_FP8, SWAP, MT_, NR_, QLIN_PF(NR_, XC_), XC_>;
+    QLIN_PICK(1, 1, 0) QLIN_PICK(1, 2, 0) QLIN_PICK(1, 4, 0)
+    QLIN_PICK(2, 1, 0) QLIN_PICK(2, 2, 0) QLIN_PICK(2, 4, 0)
+    QLIN_PICK(1, 1, 2) QLIN_PICK(1, 2, 2) QLIN_PICK(1, 4, 2)
+    QLIN_PICK(1, 1, 4) QLIN_PICK(1, 2, 4) QLIN_PICK(1, 4, 4)
+    QLIN_PICK(1, 1, 8) QLIN_PICK(1, 2, 8) QLIN_PICK(1, 4, 8)
+#undef QLIN_PICK
+    return nullptr;
+}
+
+gemm_fn gemm_pick_fp8(bool swap, int tile_m, int nr, int xc) {
+    return swap ? pick<true>(tile_m, nr, xc) : pick<false>(tile_m, nr, xc);
+}
+
+}  // namespace qlin

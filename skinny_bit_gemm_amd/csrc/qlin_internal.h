@@ -49,6 +49,7 @@ struct Plan {
     size_t lds_bytes;
     int packed;           // split-K reduction through packed 64-bit atomics
     int fuse;             // activation quantization inside the GEMM kernel
+    int xc;               // ... with this many 8-value chunks per lane in registers
     size_t ws_bytes;          // workspace bytes (0 without split)
     size_t ws_counter_bytes;  // of which arrival counters (the rest: sums)
 };
@@ -69,8 +70,9 @@ hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, v
                             float *xs, hipStream_t s);
 hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, float *ws,
                                hipStream_t s);
-hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, bool fuse, const GemmLaunch &g,
+// xc: register chunks per lane of the in-kernel quantization (0: unfused)
+hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, int xc, const GemmLaunch &g,
                        size_t lds_bytes, hipStream_t s);
-bool gemm_variant_exists(int fmt, int tile_m, int nr, bool fuse);
+bool gemm_variant_exists(int fmt, int tile_m, int nr, int xc);
 
 }  // namespace qlin

@@ -156,8 +156,8 @@ qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out,
 // follows the pages' example heuristic of dispatching to Swap-AB below 32
 // tokens (section "Kernel Implementation") and chooses a split so that the
 // grid has about four workgroups per compute unit, with at least one K block
-// per wave; small token counts quantize inside the GEMM and combine exact
-// partitions with packed atomics.
+// per wave; small token counts quantize inside the GEMM (where the tile's
+// rows fit its registers) and combine exact partitions with packed atomics.
 void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
     qlin_config c;
     c.tile_m = M <= 16 ? 16 : 32;
@@ -176,6 +176,8 @@ void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
     const bool exact = fmt == QLIN_W8A8_INT8 || (fmt == QLIN_FP8_DYNAMIC && K <= 40960);
     c.reduce = exact && M <= 8 ? 1 : 0;
     c.fuse_quant = M <= 4 && c.tile_m == 16 ? 1 : 0;
+    Plan p;
+    if (c.fuse_quant && make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) c.fuse_quant = 0;
     *out = c;
 }
 

@@ -9,9 +9,9 @@ graph replay).  Here the search is exhaustive over a fixed candidate grid
 (schedule, tile, split factor, wave layout); each candidate is timed as a
 hipGraph of back-to-back layers (qlin_linear: quantize + GEMM) over distinct
 weight copies (>= 1 GiB in total, so the Infinity Cache cannot hold them).
-A coarse pass over the schedule grid, then the best few with each split-K
-reduction and with the quantization fused or not, then the best of those
-again with more replays.
+A coarse pass over the schedule grid (each schedule with the quantization
+in its own kernel and fused into the GEMM), then the best few with each
+split-K reduction, then the best of those again with more replays.
 
 Usage:
   python -m skinny_bit_gemm_amd.tune --shape fp8_dynamic,4096,2048 ... \\
@@ -43,8 +43,9 @@ def exact_format(fmt, K):
 
 
 def candidates(fmt, M, N, K):
-    """Base grid: schedule, tile, split and wave layout (slice reduction,
-    separate quantize kernel)."""
+    """Base grid: schedule, tile, split and wave layout, each with the
+    quantization in a separate kernel and (where the tile's rows fit the
+    kernel's registers) inside the GEMM; slice reduction."""
     nkb = -(-K // 128)
     seen = set()
     out = []
@@ -57,27 +58,25 @@ def candidates(fmt, M, N, K):
                 key = (swap, tn, waves, kw, kbs)
                 if key in seen or kbs < kw:
                     continue
-                c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, 0)
-                if q.qlin_validate_config(fmt, M, N, K, c) != 0:
-                    continue
                 wgs = -(-N // tn) * -(-M // tile_m) * eff
                 if wgs < 16 or wgs > 16384:
                     continue
                 seen.add(key)
-                out.append(c)
+                for fuse in ((0, 1) if tile_m == 16 else (0,)):
+                    c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, fuse)
+                    if q.qlin_validate_config(fmt, M, N, K, c) == 0:
+                        out.append(c)
     return out
 
 
 def variants(fmt, M, N, K, c):
-    """The same schedule with each split-K reduction and quantize placement."""
+    """The same schedule with each split-K reduction."""
     out = []
     reds = [0, 1] if (c.split_k > 1 and exact_format(fmt, K)) else [0]
-    fuses = [0, 1] if c.tile_m == 16 else [0]
     for r in reds:
-        for f in fuses:
-            v = q.make_config(c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves, r, f)
-            if q.qlin_validate_config(fmt, M, N, K, v) == 0:
-                out.append(v)
+        v = q.make_config(c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves, r, c.fuse_quant)
+        if q.qlin_validate_config(fmt, M, N, K, v) == 0:
+            out.append(v)
     return out
 
 
@@ -214,7 +213,7 @@ def main(argv=None):
         f.write("# measured on MI355X by skinny_bit_gemm_amd.tune (hipGraph replay, rotating weights)\n")
         f.write("# format N K M swap_ab split_k tile_m tile_n waves k_waves reduce fuse_quant\n")
         f.write("# (times are of the whole layer, quantize + GEMM; best_by_class in the report\n"
-                "#  compares schedules with a separate quantize kernel and slice reduction)\n")
+                "#  compares the schedules' best coarse times, slice reduction)\n")
         for k in sorted(entries):
             f.write(" ".join([k[0], str(k[1]), str(k[2]), str(k[3])] + entries[k]) + "\n")
     if args.report:

@@ -124,12 +124,16 @@ def check_layer(fmt, M, N, K, x, w, c, ldx=None):
         assert np.array_equal(yi.cpu().numpy(), acc), "int32 accumulators differ"
 
 
+# In-kernel quantization holds the tile's activation rows (8-value chunks,
+# whole rows padded to 64 chunks for the per-token formats, the K range for
+# the block format) in at most 8 register chunks per thread: 16 rows of
+# K = 1536 need 8 waves.
 LAYER_CFGS = {
-    "fused": cfg(1, 1, 16, 32, 4, 4, fuse=1),
+    "fused": cfg(1, 1, 16, 32, 8, 8, fuse=1),
     "fused_std": cfg(0, 1, 16, 64, 8, 4, fuse=1),
-    "fused_split": cfg(1, 4, 16, 32, 4, 2, fuse=1),
+    "fused_split": cfg(1, 4, 16, 32, 8, 4, fuse=1),
     "fused_split_std": cfg(0, 3, 16, 16, 8, 8, fuse=1),
-    "fused_nr4": cfg(1, 2, 16, 64, 1, 1, fuse=1),
+    "fused_nr4": cfg(1, 2, 16, 256, 8, 2, fuse=1),
     "unfused": cfg(1, 2, 16, 32, 4, 4),
     "unfused_m32": cfg(0, 2, 32, 64, 4, 2),
 }
@@ -146,15 +150,31 @@ def test_linear_fused_and_unfused(fmt, name, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
-def test_linear_fused_packed_phases_and_stride(fmt):
-    """Fused quantization with packed reduction, with LDS phases (16 rows x
-    8192 codes exceed one stage) and a row stride larger than K."""
-    M, N, K = 16, 256, 8192
-    x = wl.activations(fmt, N, K, M)
+def test_linear_fused_few_waves(fmt):
+    """In-kernel quantization with 1 and 2 waves (4 and 8 register chunks
+    per thread), and the rejection of a tile whose rows do not fit."""
+    N, K = 512, 1536
+    for M, c in ((1, cfg(1, 2, 16, 64, 1, 1, fuse=1)), (3, cfg(1, 1, 16, 32, 2, 2, fuse=1))):
+        x = wl.activations(fmt, N, K, M)
+        w = wl.random_weights(N, K, 90 + M)
+        check_layer(fmt, M, N, K, x, w, c)
+    assert q.qlin_validate_config(fmt, 16, N, K, cfg(1, 2, 16, 64, 1, 1, fuse=1)) == q.QLIN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_linear_fused_packed_stride_and_phases(fmt):
+    """Fused quantization with packed reduction and a row stride larger than
+    K; unfused with LDS phases (16 rows x 8192 codes exceed one stage), where
+    the fused form is rejected."""
+    N, K = 256, 8192
     w = wl.random_weights(N, K, 61)
     red = 1 if fmt != wl.BLOCK_FP8 else 0
-    check_layer(fmt, M, N, K, x, w, cfg(1, 1, 16, 32, 4, 2, fuse=1), ldx=K + 32)
-    check_layer(fmt, M, N, K, x, w, cfg(1, 2, 16, 64, 4, 4, reduce=red, fuse=1), ldx=K + 32)
+    x4 = wl.activations(fmt, N, K, 4)
+    check_layer(fmt, 4, N, K, x4, w, cfg(1, 1, 16, 64, 8, 2, fuse=1), ldx=K + 32)
+    check_layer(fmt, 4, N, K, x4, w, cfg(1, 2, 16, 64, 8, 4, reduce=red, fuse=1), ldx=K + 32)
+    x16 = wl.activations(fmt, N, K, 16)
+    check_layer(fmt, 16, N, K, x16, w, cfg(1, 1, 16, 32, 4, 2), ldx=K + 32)
+    assert q.qlin_validate_config(fmt, 16, N, K, cfg(1, 1, 16, 64, 8, 2, fuse=1)) == q.QLIN_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
