@@ -39,7 +39,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--detail", default=None, help="write per-shape GEMM timings (JSON) here")
+    ap.add_argument("--sweep", default=None,
+                    help="instead of the step: time the crossover sweep (8B-class shapes, forced "
+                         "schedules and the table's pick) and write it (JSON) here")
+    ap.add_argument("--sweep-formats", default="fp8_dynamic,w8a8_int8,block_fp8")
+    ap.add_argument("--sweep-m", default="1,2,4,8,16,24,32,64,128,256,512")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement (1 GiB buffer)")
+    ap.add_argument("--detail", default=None,
+                    help="write per-shape timings of the whole linear and of its GEMM kernel (JSON) here")
     ap.add_argument("--gemm-only-steps", type=int, default=None,
                     help="replay only the GEMM graphs this many times (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -81,18 +89,50 @@ class Linear:
         q.qlin_gemm(self.fmt, self.M, self.N, self.K, self.xq, self.xs, self.wq if wq is None else wq,
                     self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work, stream=stream)
 
+    @property
+    def fused(self):
+        return bool(self.cfg.fuse_quant)
+
+    def kernel(self, stream):
+        """The step's GEMM kernel of this linear, as the step runs it: the
+        fused quantize + GEMM kernel where the table fuses them, else the
+        GEMM kernel alone (its codes come from the step's quantize kernel)."""
+        if self.fused:
+            self.layer(stream)
+        else:
+            self.gemm(stream)
+
+    @property
+    def kernel_bytes(self):
+        return self.bytes + (self.qbytes if self.fused else 0)
+
+
+# the device code of the path (GEMM and quantization kernels)
+KERNEL_SOURCES = ["skinny_bit_gemm_amd/csrc/" + f for f in (
+    "qlin_device.h", "qlin_gemm.h", "qlin_gemm_fp8.hip", "qlin_gemm_i8.hip", "qlin_gemm_block.hip",
+    "qlin_kernels.hip")]
+TABLE = "skinny_bit_gemm_amd/tables/gfx950.tbl"
+
+
+def source_digests():
+    """sha256 of the kernel sources (concatenated in a fixed order) and of
+    the selection table."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest(), hashlib.sha256(open(os.path.join(ROOT, TABLE), "rb").read()).hexdigest()
+
 
 def measured_traffic(workload):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
     or None when there is none or the kernels or the table changed since."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = lambda p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha("skinny_bit_gemm_amd/csrc/qlin_kernels.hip") or \
-            rec.get("table_sha256") != sha("skinny_bit_gemm_amd/tables/gfx950.tbl"):
+    ksha, tsha = source_digests()
+    if rec.get("kernel_source_sha256") != ksha or rec.get("table_sha256") != tsha:
         return None
     return rec
 
@@ -149,6 +189,90 @@ def cpu_baseline(fmt, layers, Ms, budget_s):
     }
 
 
+MFMA_PEAK_TFLOPS = 5000.0   # dense fp8 / int8 matrix-core peak of MI355X
+
+
+def sweep_configs(q, fmt, M):
+    """The forced schedules of the crossover sweep (Standard, Swap-AB,
+    Split-K 2..16) and the selection table's pick (None)."""
+    tm = 16 if M <= 16 else 32
+    out = {"standard": q.make_config(0, 1, tm, 64, 4, 2), "swap_ab": q.make_config(1, 1, tm, 64, 4, 2)}
+    for sk in (2, 4, 8, 16):
+        out[f"splitk{sk}"] = q.make_config(sk % 4 == 0, sk, tm, 64, 4, 2)
+    out["table"] = None
+    return out
+
+
+def crossover_sweep(path, fmts, Ms):
+    """GEMM time of every sweep schedule on the 8B-class shapes, each timed
+    as a hipGraph of launches over >= 1 GiB of rotating weight copies."""
+    import torch
+    import skinny_bit_gemm_amd as q
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    q.lib()
+    st = torch.cuda.Stream()
+    rows = []
+    with torch.cuda.stream(st):
+        for fmt in fmts:
+            for L in wl.DENSE_8B:
+                N, K = L.N, L.K
+                w = torch.from_numpy(wl.weights(fmt, N, K)).to(dev)
+                wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+                ws = torch.empty(q.scales_shape(fmt, N, K, True), dtype=torch.float32, device=dev)
+                q.qlin_quantize_weight(fmt, N, K, w, wq, ws, stream=st)
+                del w
+                R = max(2, -(-(1 << 30) // (N * K)))
+                copies = [wq.clone() for _ in range(R)]
+                for M in Ms:
+                    x = torch.from_numpy(wl.activations(fmt, N, K, M).view("int16")).to(dev)
+                    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                    xs = torch.empty(q.scales_shape(fmt, M, K, False), dtype=torch.float32, device=dev)
+                    q.qlin_quantize_act(fmt, M, K, x, K, xq, xs, stream=st)
+                    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                    for name, c in sweep_configs(q, fmt, M).items():
+                        cfg = c if c is not None else q.qlin_select_variant(fmt, M, N, K)
+                        work = torch.zeros(max(256, q.qlin_workspace_bytes(fmt, M, N, K, cfg)),
+                                           dtype=torch.uint8, device=dev)
+                        run = lambda: [q.qlin_gemm(fmt, M, N, K, xq, xs, wc, ws, y, q.QLIN_OUT_BF16, cfg, work,
+                                                   stream=st) for wc in copies]
+                        run()
+                        g = capture(st, run)
+                        q.qlin_graph_launch(g, st)
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(st)
+                        for _ in range(3):
+                            q.qlin_graph_launch(g, st)
+                        e1.record(st)
+                        torch.cuda.synchronize()
+                        q.qlin_graph_destroy(g)
+                        us = e0.elapsed_time(e1) * 1e3 / (3 * R)
+                        nbytes = wl.algorithmic_bytes(fmt, M, N, K)
+                        tf = wl.flops(M, N, K) / us / 1e6
+                        rows.append({"format": wl.FORMAT_NAMES[fmt], "layer": L.name, "N": N, "K": K, "M": M,
+                                     "schedule": name, "cfg": cfg.as_dict(), "us": round(us, 3),
+                                     "TFLOPs": round(tf, 2), "GBps": round(nbytes / us / 1e3, 1),
+                                     "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 4),
+                                     "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+                        del work
+                    print(f"[sweep] {wl.FORMAT_NAMES[fmt]} {L.name} M={M}: " + ", ".join(
+                        f"{r['schedule']} {r['us']:.1f}us" for r in rows if r["M"] == M and r["N"] == N
+                        and r["K"] == K and r["format"] == wl.FORMAT_NAMES[fmt]), file=sys.stderr, flush=True)
+                del copies, wq, ws
+                torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(rows, f, indent=1)
+    best = {}
+    for r in rows:
+        k = (r["format"], r["layer"], r["M"])
+        if k not in best or r["us"] < best[k]["us"]:
+            best[k] = r
+    return {"mode": "crossover_sweep", "points": len(rows), "file": path,
+            "best_frac_mfma_at_512": {f: max((b["frac_mfma"] for k, b in best.items() if k[0] == f and k[2] == 512),
+                                             default=None) for f in sorted({k[0] for k in best})}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -162,6 +286,11 @@ def main():
 
     if args.workload not in wl.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; choose from {sorted(wl.WORKLOADS)}")
+    if args.sweep:
+        fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
+        print(json.dumps(crossover_sweep(args.sweep, fmts, [int(m) for m in args.sweep_m.split(",")])),
+              flush=True)
+        return
     fmt, layers, Ms = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -201,14 +330,17 @@ def main():
         # eager once (also checks every launch is accepted), then capture
         for lin in sets[0]:
             lin.layer(stream)
-            lin.gemm(stream)
+            lin.kernel(stream)
+        for ls in sets[1:]:
+            for lin in ls:
+                lin.layer(stream)
         torch.cuda.synchronize()
         step_graphs = [capture(stream, lambda ls=ls: [l.layer(stream) for l in ls]) for ls in sets]
-        gemm_graphs = [capture(stream, lambda ls=ls: [l.gemm(stream) for l in ls]) for ls in sets]
+        gemm_graphs = [capture(stream, lambda ls=ls: [l.kernel(stream) for l in ls]) for ls in sets]
         torch.cuda.synchronize()
 
         step_bytes = sum(l.bytes + l.qbytes for l in sets[0])
-        gemm_bytes = sum(l.bytes for l in sets[0])
+        gemm_bytes = sum(l.kernel_bytes for l in sets[0])
         step_flops = sum(l.flops for l in sets[0])
         n_gemm = len(sets[0])
 
@@ -231,7 +363,8 @@ def main():
         torch.cuda.synchronize()
         ms_step = e0.elapsed_time(e1) / args.steps
 
-        # GEMM launches alone (same launches, same order), for the roofline
+        # the step's GEMM kernels alone (same launches, same order; the fused
+        # ones include their quantization), for the roofline
         g0 = torch.cuda.Event(enable_timing=True)
         g1 = torch.cuda.Event(enable_timing=True)
         for i in range(2):
@@ -245,11 +378,11 @@ def main():
 
         detail = []
         if args.detail:
-            # per (M, layer): a graph of that GEMM over every weight copy
-            for j in range(n_gemm):
-                ls = [s_[j] for s_ in sets]
+            # per (M, layer): graphs of the whole linear and of its GEMM
+            # kernel over every weight copy
+            def per_launch_us(ls, fn):
                 reps = max(1, -(-64 // len(ls)))
-                g = capture(stream, lambda ls=ls: [l.gemm(stream) for _ in range(reps) for l in ls])
+                g = capture(stream, lambda: [fn(l) for _ in range(reps) for l in ls])
                 q.qlin_graph_launch(g, stream)
                 d0 = torch.cuda.Event(enable_timing=True)
                 d1 = torch.cuda.Event(enable_timing=True)
@@ -258,13 +391,21 @@ def main():
                     q.qlin_graph_launch(g, stream)
                 d1.record(stream)
                 torch.cuda.synchronize()
-                us = d0.elapsed_time(d1) * 1e3 / (5 * reps * len(ls))
                 q.qlin_graph_destroy(g)
+                return d0.elapsed_time(d1) * 1e3 / (5 * reps * len(ls))
+
+            for j in range(n_gemm):
+                ls = [s_[j] for s_ in sets]
                 l0 = ls[0]
-                detail.append({"layer": l0.name, "M": l0.M, "N": l0.N, "K": l0.K, "us": round(us, 3),
-                               "GBps": round(l0.bytes / us / 1e3, 1),
-                               "TFLOPs": round(l0.flops / us / 1e6, 3),
-                               "frac_hbm": round(l0.bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                layer_us = per_launch_us(ls, lambda l: l.layer(stream))
+                kernel_us = per_launch_us(ls, lambda l: l.kernel(stream))
+                detail.append({"layer": l0.name, "M": l0.M, "N": l0.N, "K": l0.K, "fused": l0.fused,
+                               "layer_us": round(layer_us, 3),
+                               "layer_GBps": round((l0.bytes + l0.qbytes) / layer_us / 1e3, 1),
+                               "layer_TFLOPs": round(l0.flops / layer_us / 1e6, 3),
+                               "kernel_us": round(kernel_us, 3),
+                               "kernel_GBps": round(l0.kernel_bytes / kernel_us / 1e3, 1),
+                               "kernel_frac_hbm": round(l0.kernel_bytes / kernel_us / 1e3 / HBM_PEAK_GBS, 4),
                                "cfg": l0.cfg.as_dict()})
 
     for g in step_graphs + gemm_graphs:
@@ -302,11 +443,16 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "gemm_kernel (all launches of a step)",
+            "kernel": "gemm_kernel (every launch of a step; the fused ones include their quantization)",
             "avg_launch_us": round(ms_gemms * 1e3 / n_gemm, 3),
             "bytes_per_launch": round(gemm_bytes / n_gemm),
         },
     }
+    if not args.no_read_ceiling:
+        from skinny_bit_gemm_amd import probe
+        ceiling = probe.read_ceiling_gbs()
+        out["roofline"]["read_ceiling_GBps"] = round(ceiling, 1)
+        out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling, 4)
     tr = measured_traffic(args.workload)
     if tr is not None:
         out["roofline"]["traffic"] = tr["per_launch_traffic_bytes"]
@@ -314,8 +460,19 @@ def main():
         out["roofline"]["traffic_vs_algorithmic"] = round(
             tr["per_launch_traffic_bytes"] / tr["per_launch_algorithmic_bytes"], 3)
     if detail:
+        import math
+        ceiling = out["roofline"].get("read_ceiling_GBps")
+        for d in detail:
+            if ceiling:
+                d["kernel_frac_read_ceiling"] = round(d["kernel_GBps"] / ceiling, 4)
+        summary = {
+            "workload": args.workload,
+            "geomean_layer_GBps": round(math.exp(sum(math.log(d["layer_GBps"]) for d in detail) / len(detail)), 1),
+            "geomean_kernel_GBps": round(math.exp(sum(math.log(d["kernel_GBps"]) for d in detail) / len(detail)), 1),
+            "read_ceiling_GBps": ceiling,
+        }
         with open(args.detail, "w") as f:
-            json.dump(detail, f, indent=1)
+            json.dump({"summary": summary, "shapes": detail}, f, indent=1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(fmt, layers, Ms, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -89,7 +89,8 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     // activation codes of the tile's existing token rows (128 bytes per row
     // and K block) plus, for the block format, one fp32 scale per row and block
     const int rows = M < c.tile_m ? M : c.tile_m;
-    const int per_block = rows * kGroup + (fmt == QLIN_BLOCK_FP8 ? rows * 4 : 0);
+    // (the staging gives each group of rows an odd number of 16-byte slots)
+    const int per_block = (rows | 1) * kGroup + (fmt == QLIN_BLOCK_FP8 ? rows * 4 : 0);
     int pb = kLdsBudget / per_block;
     if (pb > p->kb_per_split) pb = p->kb_per_split;
     p->phase_blocks = pb;

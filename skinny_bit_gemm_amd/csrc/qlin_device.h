@@ -88,13 +88,12 @@ __device__ __forceinline__ float absmax8(uint4 v) {
     return __uint_as_float(m << 16);
 }
 
-// bf16 x 8 -> 8 codes packed little-endian into two words.  The values are
-// converted one after another: each IEEE division holds a scalar register
-// pair for its scaling flag, and left to interleave many of them the
-// scheduler runs out of scalar registers (a wave issues one vector
-// instruction at a time either way).
+// bf16 x 8 -> 8 codes packed little-endian into two words, one IEEE
+// division per value.  The values are converted one after another: each
+// division holds a scalar register pair for its scaling flag, and left to
+// interleave many of them the scheduler runs out of scalar registers.
 template <int FMT>
-__device__ __forceinline__ uint2 quant8(uint4 v, float s) {
+__device__ __forceinline__ uint2 quant8_ieee(uint4 v, float s) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t out[2] = {0, 0};
 #pragma unroll
@@ -105,6 +104,68 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s) {
         __builtin_amdgcn_sched_barrier(0);
     }
     return make_uint2(out[0], out[1]);
+}
+
+// Scales at least this large take the reciprocal route below.
+constexpr float kFastScaleMin = 0x1p-60f;
+
+// a / s for a >= 0, from y = 1 / s (an IEEE division, correctly rounded):
+// q0 = a*y is within 1.5 ulp of a/s, one residual correction makes it
+// faithful, and a second one (Markstein's theorem: a faithful quotient, a
+// reciprocal within 2^-24 relative error, exact FMA residual) rounds it
+// correctly, so the result is the IEEE quotient a / s.  Only when a is so
+// small (below about 2^-102) that the residuals lose bits to underflow may
+// the last bit differ; with s >= 2^-60 the quotient is then below 2^-42,
+// far from the first rounding threshold of either code, so the code is the
+// same.  (Checked on gfx950 over every bf16 amax and every bf16 x <= amax,
+// for both 127 and 448: identical int8 and e4m3 codes.)
+__device__ __forceinline__ float div_by_scale(float a, float s, float y) {
+    const float q0 = a * y;
+    const float r0 = __builtin_fmaf(-s, q0, a);
+    const float q1 = __builtin_fmaf(r0, y, q0);
+    const float r1 = __builtin_fmaf(-s, q1, a);
+    return __builtin_fmaf(r1, y, q1);
+}
+
+// bf16 x 8 -> 8 codes packed little-endian into two words, given the run's
+// scale s and y = 1.0f / s.  The quotient is formed for |x| and the sign of
+// x copied onto it (the division, the rounding and the saturation are all
+// symmetric, and -0 keeps its sign as code 0x80); e4m3 codes come from the
+// matrix core's conversion instruction (round to nearest even, subnormals
+// kept; identical to e4m3_code for every fp32 of magnitude <= 448, which the
+// clamp guarantees).
+template <int FMT>
+__device__ __forceinline__ uint2 quant8(uint4 v, float s, float y) {
+    if (!(s >= kFastScaleMin)) return quant8_ieee<FMT>(v, s);   // tiny or zero scale
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t word = w[2 * h + (j >> 1)];
+            const uint32_t bits = (j & 1) ? (word & 0xFFFF0000u) : (word << 16);
+            float q = div_by_scale(__uint_as_float(bits & 0x7FFFFFFFu), s, y);
+            if constexpr (FMT == FMT_I8) q = __builtin_rintf(fminf(q, 127.0f));
+            else q = fminf(q, 448.0f);
+            t[j] = __uint_as_float(__float_as_uint(q) | (bits & 0x80000000u));
+        }
+        if constexpr (FMT == FMT_I8) {
+            out[h] = ((uint32_t)(int32_t)t[0] & 0xFFu) | (((uint32_t)(int32_t)t[1] & 0xFFu) << 8) |
+                     (((uint32_t)(int32_t)t[2] & 0xFFu) << 16) | ((uint32_t)(int32_t)t[3] << 24);
+        } else {
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], pk, true);
+            out[h] = (uint32_t)pk;
+        }
+    }
+    return make_uint2(out[0], out[1]);
+}
+
+// y = 1 / s for quant8 (any value for a scale that takes the IEEE route)
+__device__ __forceinline__ float recip_scale(float s) {
+    return s >= kFastScaleMin ? 1.0f / s : 0.0f;
 }
 
 }  // namespace qlin

@@ -42,10 +42,13 @@ namespace qlin {
 //
 // Activations.  The workgroup's token rows for its K range are staged once
 // in LDS, only the rows that exist (R = min(TM, M - m0)), laid out as
-// [K block][half][quarter][row][16 bytes]: the 16 lanes of a quarter read 16
+// [K block][half][quarter][row][16 bytes] with Rs = R | 1 row slots per
+// (block, half, quarter) group: the 16 lanes of a quarter read 16
 // consecutive 16-byte chunks, so the two ds_read_b128 per block are free of
-// bank conflicts.  Lanes whose row is past R use zeros.  When R x (K range)
-// does not fit the LDS budget the range is processed in phases.
+// bank conflicts, and the odd group stride spreads the staging writes (which
+// walk along K within a row, one group per 16 bytes) over the banks.  Lanes
+// whose row is past R use zeros.  When Rs x (K range) does not fit the LDS
+// budget the range is processed in phases.
 //
 // Order of the memory requests.  The vector memory counter a wave waits on
 // counts requests in issue order, so a wait for one load is a wait for every
@@ -164,9 +167,9 @@ __device__ __forceinline__ void wait_memory_idle() {
 
 // byte offset in the LDS staging layout [block][half][quarter][row][16B] of
 // 8-byte chunk cl (0, 1, ... along the K range) of row `row` (R rows)
-__device__ __forceinline__ int stage_offset8(int cl, int row, int R) {
+__device__ __forceinline__ int stage_offset8(int cl, int row, int Rs) {
     const int b = cl >> 4, cc = cl & 15, u = cc >> 1;
-    return (((b * 2 + (u & 1)) * 4 + (u >> 1)) * R + row) * 16 + (cc & 1) * 8;
+    return (((b * 2 + (u & 1)) * 4 + (u >> 1)) * Rs + row) * 16 + (cc & 1) * 8;
 }
 
 // activation 16-byte units staged per thread straight from registers (the
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
     __shared__ float s_rowscale[16 * MT];
+    __shared__ float s_rowrecip[16 * MT];
     __shared__ float s_seg[FUSE ? XC * kMaxWaves : 1];   // per-token amax of 64-chunk segments
 
     const int lane = threadIdx.x & 63;
@@ -199,6 +203,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     const int r16 = lane & 15, quarter = lane >> 4;
     const int G = (K + kGroup - 1) / kGroup;
     const int R = min(16 * MT, M - m0);   // token rows that exist in this tile
+    const int Rs = R | 1;                  // row groups of the LDS staging, an odd number of rows
     // fused path: the first column of workgroups also stores the codes and
     // scales it produces (every workgroup of a row of tiles produces the same)
     const bool writer = FUSE && blockIdx.x == 0;
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     // (rows past R read an existing row, and their data is replaced by zeros)
     int lds_lo[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) lds_lo[mt] = (quarter * R + (mt * 16 + r16 < R ? mt * 16 + r16 : 0)) * 16;
+    for (int mt = 0; mt < MT; ++mt) lds_lo[mt] = (quarter * Rs + (mt * 16 + r16 < R ? mt * 16 + r16 : 0)) * 16;
 
     acc_t acc[NR][MT];
 #pragma unroll
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         const int nblk = min(kb_end - pb0, g.phase_blocks);
         // this wave's blocks of the phase are kw, kw + kstep, ... (a uniform count)
         const int nmine = kw < nblk ? (nblk - kw + kstep - 1) / kstep : 0;
-        float *s_scale = reinterpret_cast<float *>(smem + (size_t)g.phase_blocks * kGroup * R);
+        float *s_scale = reinterpret_cast<float *>(smem + (size_t)g.phase_blocks * kGroup * Rs);
 
         // ---- 1. activation requests
         // fused: the tile's R rows x cn chunk positions of 8 values (per-token
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 const int b = rest % nblk, row = rest / nblk;
                 const int k = (pb0 + b) * kGroup + c * 16;
                 sv[s] = load16(qrs, it < items && k < K ? (uint32_t)(row * K + k) : kOutOfRange);
-                spos[s] = it < items ? (((b * 2 + (c & 1)) * 4 + (c >> 1)) * R + row) * 16 : -1;
+                spos[s] = it < items ? (((b * 2 + (c & 1)) * 4 + (c >> 1)) * Rs + row) * 16 : -1;
             }
             if constexpr (FMT == FMT_BLOCK) {
                 const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(g.xs + (int64_t)m0 * G, (uint32_t)(R * G * 4));
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         if constexpr (FUSE) {
             const int kc0 = kb_begin * 16, kc1 = kb_end * 16;   // chunks staged (absolute)
             auto stage8 = [&](int row, int c, uint2 codes) {   // c absolute
-                *reinterpret_cast<uint2 *>(smem + stage_offset8(c - kc0, row, R)) = codes;
+                *reinterpret_cast<uint2 *>(smem + stage_offset8(c - kc0, row, Rs)) = codes;
                 if (writer && c < nchunk)
                     *reinterpret_cast<uint2 *>(g.xq_out + (int64_t)(m0 + row) * K + c * 8) = codes;
             };
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                     for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
                     const float sc = amax == 0.0f ? 0.0f : amax / 448.0f;
                     if (row < R) {
-                        stage8(row, c_lo + c, quant8<FMT>(xr[i], sc));
+                        stage8(row, c_lo + c, quant8<FMT>(xr[i], sc, recip_scale(sc)));
                         if ((c & 15) == 0) {
                             s_scale[(c >> 4) * R + row] = sc;
                             if (writer) g.xs_out[(int64_t)(m0 + row) * G + kb_begin + (c >> 4)] = sc;
@@ -387,19 +392,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                     }
                 }
                 __syncthreads();
+                // one thread per row: the row's amax, scale and reciprocal
+                if ((int)threadIdx.x < R) {
+                    const int row = threadIdx.x;
+                    float amax = 0.0f;
+                    for (int sg = 0; sg < segs; ++sg) amax = fmaxf(amax, s_seg[row * segs + sg]);
+                    const float sc = amax == 0.0f ? 0.0f : amax / qmax_of<FMT>();
+                    s_rowscale[row] = sc;
+                    s_rowrecip[row] = recip_scale(sc);
+                    if (writer && blockIdx.z == 0) g.xs_out[m0 + row] = sc;
+                }
+                __syncthreads();
                 int row = row0, c = c0;
 #pragma unroll
                 for (int i = 0; i < XC; ++i) {
-                    if (row < R) {
-                        float amax = 0.0f;
-                        for (int sg = 0; sg < segs; ++sg) amax = fmaxf(amax, s_seg[row * segs + sg]);
-                        const float sc = amax == 0.0f ? 0.0f : amax / qmax_of<FMT>();
-                        if (c == 0) {
-                            s_rowscale[row] = sc;
-                            if (writer && blockIdx.z == 0) g.xs_out[m0 + row] = sc;
-                        }
-                        if (c >= kc0 && c < kc1) stage8(row, c, quant8<FMT>(xr[i], sc));
-                    }
+                    if (row < R && c >= kc0 && c < kc1)
+                        stage8(row, c, quant8<FMT>(xr[i], s_rowscale[row], s_rowrecip[row]));
                     next_slot(row, c);
                 }
             }
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             auto put = [&](int it, uint4 v) {
                 const int c = it & 7, rest = it >> 3;
                 const int b = rest % nblk, row = rest / nblk;
-                *reinterpret_cast<uint4 *>(smem + (((b * 2 + (c & 1)) * 4 + (c >> 1)) * R + row) * 16) = v;
+                *reinterpret_cast<uint4 *>(smem + (((b * 2 + (c & 1)) * 4 + (c >> 1)) * Rs + row) * 16) = v;
             };
 #pragma unroll
             for (int s = 0; s < kStageRegs; ++s)
@@ -437,13 +445,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             const int b = kw + jb * kstep;
             // activation fragments of this block (zeros past row R; the read
             // address is clamped to an existing row)
-            const int boff = __builtin_amdgcn_readfirstlane(b * 8 * R * 16);   // uniform
+            const int boff = __builtin_amdgcn_readfirstlane(b * 8 * Rs * 16);   // uniform
             v8i xf[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const bool live = mt * 16 + r16 < R;
                 const uint4 lo = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + boff);
-                const uint4 hi = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + 4 * R * 16 + boff);
+                const uint4 hi = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + 4 * Rs * 16 + boff);
                 xf[mt] = join(select4(live, lo), select4(live, hi));
             }
             if constexpr (FMT == FMT_BLOCK) {

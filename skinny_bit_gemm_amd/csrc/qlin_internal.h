@@ -13,7 +13,7 @@ namespace qlin {
 
 constexpr int kGroup = 128;          // K block: one fp8 MFMA, one 1x128 scale group
 constexpr int kMaxWaves = 8;         // waves per workgroup
-constexpr int kLdsBudget = 64 * 1024; // bytes of LDS a GEMM workgroup may use
+constexpr int kLdsBudget = 78 * 1024; // bytes of LDS a GEMM workgroup may use (two fit a CU)
 constexpr int kMaxSplit = 64;
 
 // Everything a GEMM launch needs, resolved on the host.

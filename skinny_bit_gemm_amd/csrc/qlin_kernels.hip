@@ -48,17 +48,18 @@ __global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(const uint16
 #pragma unroll
     for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
     const float s = amax == 0.0f ? 0.0f : amax / qmax_of<FMT>();
+    const float y = recip_scale(s);
     if (threadIdx.x == 0) xs[m] = s;
     if constexpr (CPT > 0) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const int c = threadIdx.x + j * kQuantThreads;
-            if (c < nch) *reinterpret_cast<uint2 *>(qrow + c * 8) = quant8<FMT>(v[j], s);
+            if (c < nch) *reinterpret_cast<uint2 *>(qrow + c * 8) = quant8<FMT>(v[j], s, y);
         }
     } else {
         for (int c = threadIdx.x; c < nch; c += kQuantThreads)
             *reinterpret_cast<uint2 *>(qrow + c * 8) =
-                quant8<FMT>(*reinterpret_cast<const uint4 *>(row + c * 8), s);
+                quant8<FMT>(*reinterpret_cast<const uint4 *>(row + c * 8), s, y);
     }
 }
 
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void quant_group_kernel(const uint16_t *__rest
     const float s = amax == 0.0f ? 0.0f : amax / 448.0f;
     if (!live) return;
     if (j == 0) xs[(int64_t)m * G + g] = s;
-    *reinterpret_cast<uint2 *>(xq + (int64_t)m * K + g * kGroup + j * 8) = quant8<FMT_BLOCK>(v, s);
+    *reinterpret_cast<uint2 *>(xq + (int64_t)m * K + g * kGroup + j * 8) = quant8<FMT_BLOCK>(v, s, recip_scale(s));
 }
 
 // ------------------------------------------------------- weight quantization

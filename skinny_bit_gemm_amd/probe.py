@@ -1,0 +1,59 @@
+"""Binding of the measurement aid libqlin_probe.so (include/qlin_probe.h):
+the streaming-read ceiling of HBM that bench.py reports next to the GEMM."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROBE_LIB_PATH = os.path.join(HERE, "libqlin_probe.so")
+EXPORTS = ("qlin_probe_read",)
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build it with "
+                               "`python -m skinny_bit_gemm_amd.build`")
+        import torch  # noqa: F401  (bind to torch's HIP runtime, as libqlin.so does)
+        L = ctypes.CDLL(PROBE_LIB_PATH)
+        L.qlin_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+        L.qlin_probe_read.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def qlin_probe_read(buf, nbytes, sink, blocks, stream=None):
+    """Enqueue one streaming read of nbytes of buf; returns the status code."""
+    from . import _ptr, _stream
+    return lib().qlin_probe_read(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream))
+
+
+def read_ceiling_gbs(nbytes=1 << 30, grids=(256, 512, 8192, 32768), reps=10):
+    """GB/s of a plain read of a fresh nbytes buffer: the best over a few
+    grid sizes (one workgroup per compute unit streams best on MI355X) and
+    reps timed launches each."""
+    import torch
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
+    st = torch.cuda.Stream()
+    best = None
+    with torch.cuda.stream(st):
+        for blocks in grids:
+            if qlin_probe_read(buf, nbytes, sink, blocks, st) != 0:
+                raise RuntimeError("qlin_probe_read was rejected")
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                qlin_probe_read(buf, nbytes, sink, blocks, st)
+                e1.record(st)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) * 1e-3
+                best = t if best is None else min(best, t)
+    del buf, sink
+    return nbytes / best / 1e9

@@ -1,6 +1,8 @@
 """The C ABI on the host (no GPU): the library loads, exports every symbol
 include/qlin.h declares, rejects bad arguments before any HIP call, and
-reads / rejects selection tables.  No call here reaches a kernel launch."""
+reads / rejects selection tables; the same for the measurement aid
+libqlin_probe.so (include/qlin_probe.h).  No call here reaches a kernel
+launch."""
 import ctypes
 import os
 import re
@@ -25,8 +27,8 @@ def _restore_table():
         q.qlin_load_table(q.TABLE_PATH)
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b(qlin_\w+)\s*\(", text)
     return sorted(set(names))
@@ -39,6 +41,21 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"{n} declared in qlin.h but not exported"
     assert set(names) == set(q.EXPORTS)
+
+
+def test_probe_library_exports_and_validates():
+    from skinny_bit_gemm_amd import probe
+    L = probe.lib()
+    names = declared_functions(os.path.join(ROOT, "include", "qlin_probe.h"))
+    assert set(names) == set(probe.EXPORTS)
+    for n in names:
+        assert hasattr(L, n)
+    # rejected before any HIP call: null, misaligned, ragged size, bad grid
+    assert probe.qlin_probe_read(0, 1 << 20, A, 64, 0) == 1
+    assert probe.qlin_probe_read(A + 4, 1 << 20, A, 64, 0) == 1
+    assert probe.qlin_probe_read(A, (1 << 20) + 8, A, 64, 0) == 1
+    assert probe.qlin_probe_read(A, 1 << 20, A, 0, 0) == 1
+    assert probe.qlin_probe_read(A, 1 << 20, A, 70000, 0) == 1
 
 
 def test_abi_version_and_status_strings():
