@@ -194,11 +194,15 @@ MFMA_PEAK_TFLOPS = 5000.0   # dense fp8 / int8 matrix-core peak of MI355X
 
 def sweep_configs(q, fmt, M):
     """The forced schedules of the crossover sweep (Standard, Swap-AB,
-    Split-K 2..16) and the selection table's pick (None)."""
+    Split-K 2..16, the large-M kernel) and the selection table's pick (None)."""
     tm = 16 if M <= 16 else 32
     out = {"standard": q.make_config(0, 1, tm, 64, 4, 2), "swap_ab": q.make_config(1, 1, tm, 64, 4, 2)}
     for sk in (2, 4, 8, 16):
         out[f"splitk{sk}"] = q.make_config(sk % 4 == 0, sk, tm, 64, 4, 2)
+    # the large-M kernel (64- / 128-token tiles), with and without split-K
+    for tmb in (64, 128):
+        for sk in (1, 2, 4):
+            out[f"large_m{tmb}" + (f"_split{sk}" if sk > 1 else "")] = q.make_config(0, sk, tmb, 128, 4, 1)
     out["table"] = None
     return out
 

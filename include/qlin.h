@@ -84,7 +84,10 @@ typedef enum {
  *   split_k    number of K partitions handled by separate workgroups, 1..64;
  *              each covers ceil(K / split_k) rounded up to 128 (the effective
  *              count can be lower).
- *   tile_m     tokens per tile: 16 or 32.
+ *   tile_m     tokens per tile: 16 or 32 (the skinny kernel), or 64 or 128
+ *              (the large-M kernel for token counts past the skinny range:
+ *              it needs tile_n 128, waves 4, k_waves 1, swap_ab 0,
+ *              reduce 0, fuse_quant 0).
  *   tile_n     output channels per workgroup: a multiple of 16, <= 256.
  *   waves      64-lane waves per workgroup: 1, 2, 4 or 8.
  *   k_waves    how many of those waves split the workgroup's K range
@@ -97,7 +100,9 @@ typedef enum {
  *              not depend on the order partitions finish in.
  *   fuse_quant qlin_linear only: 1 = each GEMM workgroup quantizes the
  *              activations it needs itself (one kernel instead of two;
- *              needs tile_m 16); ignored by qlin_gemm.                      */
+ *              needs tile_m 16, the K range in one LDS stage and the tile's
+ *              activation rows within 8 register chunks of 8 values per
+ *              thread); ignored by qlin_gemm.                               */
 typedef struct {
     int32_t swap_ab;
     int32_t split_k;

@@ -54,13 +54,26 @@ qlin_status resolve_config(qlin_format fmt, int M, int N, int K, const qlin_conf
 
 }  // namespace
 
+// workspace: [arrival counters][packed int64 sums, or one slice of 32-bit
+// partial sums per partition]; all of it is zero between calls
+static void set_workspace(Plan *p, int M, int N) {
+    if (p->nsplit > 1) {
+        p->ws_counter_bytes = align256((size_t)p->n_tiles * p->m_tiles * 4);
+        const size_t sums = p->packed ? (size_t)M * N * 8 : (size_t)p->nsplit * M * N * 4;
+        p->ws_bytes = p->ws_counter_bytes + align256(sums);
+    } else {
+        p->ws_counter_bytes = 0;
+        p->ws_bytes = 0;
+    }
+}
+
 qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c, bool fused,
                       Plan *p) {
     if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
     if (M < 1) M = 1;
     if (c.swap_ab != 0 && c.swap_ab != 1) return QLIN_ERR_INVALID_ARG;
     if (c.split_k < 1 || c.split_k > kMaxSplit) return QLIN_ERR_INVALID_ARG;
-    if (c.tile_m != 16 && c.tile_m != 32) return QLIN_ERR_INVALID_ARG;
+    if (c.tile_m != 16 && c.tile_m != 32 && c.tile_m != 64 && c.tile_m != 128) return QLIN_ERR_INVALID_ARG;
     if (c.waves != 1 && c.waves != 2 && c.waves != 4 && c.waves != 8) return QLIN_ERR_INVALID_ARG;
     if (c.k_waves < 1 || c.k_waves > c.waves || c.waves % c.k_waves != 0) return QLIN_ERR_INVALID_ARG;
     if (c.reduce != 0 && c.reduce != 1) return QLIN_ERR_INVALID_ARG;
@@ -72,6 +85,31 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
         return QLIN_ERR_INVALID_ARG;
     const bool fuse = fused && c.fuse_quant == 1;
     if (c.fuse_quant == 1 && c.tile_m != 16) return QLIN_ERR_INVALID_ARG;
+    if (c.tile_m >= 64) {
+        // The large-M kernel: 128-channel tiles, 4 waves in a 2 x 2 grid,
+        // Standard operand roles, slice reduction, static LDS.
+        if (c.tile_n != 128 || c.waves != 4 || c.k_waves != 1 || c.swap_ab != 0 || c.reduce != 0)
+            return QLIN_ERR_INVALID_ARG;
+        if (!gemm_variant_exists(fmt, c.tile_m, 0, 0)) return QLIN_ERR_INVALID_ARG;
+        p->tile_m = c.tile_m;
+        p->tile_n = 128;
+        p->nr = 0;
+        p->nw = 2;
+        p->kw = 1;
+        p->waves = 4;
+        p->fuse = 0;
+        p->xc = 0;
+        p->nkb = (K + kGroup - 1) / kGroup;
+        p->kb_per_split = (p->nkb + c.split_k - 1) / c.split_k;
+        p->nsplit = (p->nkb + p->kb_per_split - 1) / p->kb_per_split;
+        p->phase_blocks = p->kb_per_split;
+        p->lds_bytes = 0;
+        p->n_tiles = (N + 127) / 128;
+        p->m_tiles = (M + c.tile_m - 1) / c.tile_m;
+        p->packed = 0;
+        set_workspace(p, M, N);
+        return QLIN_OK;
+    }
     const int nw = c.waves / c.k_waves;
     if (c.tile_n < 16 || c.tile_n > 256 || c.tile_n % (16 * nw) != 0) return QLIN_ERR_INVALID_ARG;
     const int nr = c.tile_n / (16 * nw);
@@ -116,17 +154,8 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     p->lds_bytes = lds;
     p->n_tiles = (N + c.tile_n - 1) / c.tile_n;
     p->m_tiles = (M + c.tile_m - 1) / c.tile_m;
-    // workspace: [arrival counters][packed int64 sums, or one slice of
-    // 32-bit partial sums per partition]; all of it is zero between calls
     p->packed = p->nsplit > 1 && c.reduce == 1;
-    if (p->nsplit > 1) {
-        p->ws_counter_bytes = align256((size_t)p->n_tiles * p->m_tiles * 4);
-        const size_t sums = p->packed ? (size_t)M * N * 8 : (size_t)p->nsplit * M * N * 4;
-        p->ws_bytes = p->ws_counter_bytes + align256(sums);
-    } else {
-        p->ws_counter_bytes = 0;
-        p->ws_bytes = 0;
-    }
+    set_workspace(p, M, N);
     return QLIN_OK;
 }
 

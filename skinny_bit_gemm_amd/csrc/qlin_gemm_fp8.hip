@@ -1,12 +1,17 @@
 // qlin_gemm_fp8.hip -- the GEMM kernel variants of one format (FMT_FP8), and
 // their dispatch; one source file per format so the variants build in
 // parallel.
-#include "qlin_gemm.h"
+#include "qlin_gemm_big.h"
 
 namespace qlin {
 
 template <bool SWAP>
 static gemm_fn pick(int tile_m, int nr, int xc) {
+    // token tiles of 64 / 128: the large-M kernel (Standard operand roles)
+    if (tile_m == 64 || tile_m == 128) {
+        if (SWAP || xc != 0) return nullptr;
+        return tile_m == 64 ? gemm_big_kernel<FMT_FP8, 64> : gemm_big_kernel<FMT_FP8, 128>;
+    }
 #define QLIN_PICK(MT_, NR_, XC_) \
     if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_) return gemm_kernel<FMT_FP8, SWAP, MT_, NR_, QLIN_PF(NR_, XC_), XC_>;
     QLIN_PICK(1, 1, 0) QLIN_PICK(1, 2, 0) QLIN_PICK(1, 4, 0)

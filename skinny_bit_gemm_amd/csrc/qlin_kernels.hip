@@ -214,6 +214,13 @@ hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, int xc, const Gem
     case FMT_BLOCK: f = gemm_pick_block(swap, tile_m, nr, xc); break;
     }
     if (!f) return hipErrorInvalidValue;
+    if (tile_m >= 64) {
+        // large-M kernel: one-dimensional grid in its XCD-aware tile order
+        // (N tiles padded to a multiple of 8), static LDS
+        const unsigned n8 = (unsigned)((g.n_tiles + 7) & ~7);
+        hipLaunchKernelGGL(f, dim3(n8 * g.m_tiles * g.nsplit), dim3(256), 0, s, g);
+        return hipGetLastError();
+    }
     const dim3 grid(g.n_tiles, g.m_tiles, g.nsplit);
     const dim3 block(64 * g.nw * g.kw);
     hipLaunchKernelGGL(f, grid, block, lds_bytes, s, g);

@@ -158,8 +158,15 @@ qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out,
 // grid has about four workgroups per compute unit, with at least one K block
 // per wave; small token counts quantize inside the GEMM (where the tile's
 // rows fit its registers) and combine exact partitions with packed atomics.
+// From 128 tokens on it takes the large-M kernel (64-token tiles).
 void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
     qlin_config c;
+    if (M >= 128) {
+        // the large-M kernel, 64-token tiles, no split
+        c = qlin_config{0, 1, 64, 128, 4, 1, 0, 0};
+        *out = c;
+        return;
+    }
     c.tile_m = M <= 16 ? 16 : 32;
     c.swap_ab = M < 32 ? 1 : 0;
     c.waves = 4;

@@ -66,6 +66,17 @@ def candidates(fmt, M, N, K):
                     c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, fuse)
                     if q.qlin_validate_config(fmt, M, N, K, c) == 0:
                         out.append(c)
+    if M > 32:
+        # the large-M kernel: 64- / 128-token tiles of 128 channels
+        for tmb in (64, 128):
+            for split in (1, 2, 3, 4, 6, 8):
+                kbs = -(-nkb // split)
+                eff = -(-nkb // kbs)
+                c = q.make_config(0, eff, tmb, 128, 4, 1, 0, 0)
+                if (tmb, kbs) in seen or q.qlin_validate_config(fmt, M, N, K, c) != 0:
+                    continue
+                seen.add((tmb, kbs))
+                out.append(c)
     return out
 
 
@@ -142,6 +153,8 @@ class Bench:
 
 
 def variant_class(c):
+    if c.tile_m >= 64:
+        return "large_m"
     if c.split_k > 1:
         return "splitk"
     return "swap_ab" if c.swap_ab else "standard"
@@ -175,7 +188,7 @@ def algorithmic_bytes(fmt, M, N, K):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--shape", action="append", default=[], help="fmt,N,K")
-    ap.add_argument("--m", default="1,2,4,8,16,24,32")
+    ap.add_argument("--m", default="1,2,4,8,16,24,32,64,128,256,512")
     ap.add_argument("--out", default=os.path.join(os.path.dirname(__file__), "tables", "gfx950.tbl"))
     ap.add_argument("--merge", action="store_true", help="keep existing entries of --out")
     ap.add_argument("--report", default=None)

@@ -97,6 +97,28 @@ def test_gemm_rejects_bad_configs():
         assert q.qlin_validate_config(FP8, 4, 256, 512, c) == EINVAL
 
 
+def test_large_m_configs():
+    """Token tiles of 64 / 128 select the large-M kernel: 128-channel tiles,
+    4 waves in one K row, Standard roles, slice reduction, no in-kernel
+    quantization."""
+    for fmt in (FP8, I8, BLK):
+        for tm in (64, 128):
+            for split in (1, 3):
+                assert q.qlin_validate_config(fmt, 300, 512, 2048, q.make_config(0, split, tm, 128, 4, 1)) == OK
+        bad = [q.make_config(1, 1, 128, 128, 4, 1), q.make_config(0, 1, 128, 64, 4, 1),
+               q.make_config(0, 1, 128, 128, 8, 1), q.make_config(0, 1, 128, 128, 4, 4),
+               q.make_config(0, 2, 128, 128, 4, 1, reduce=1), q.make_config(0, 1, 128, 128, 4, 1, fuse_quant=1),
+               q.make_config(0, 1, 96, 128, 4, 1)]
+        for c in bad:
+            assert q.qlin_validate_config(fmt, 300, 512, 2048, c) == EINVAL, (fmt, c)
+    # slices: counters for every (M tile, 128-channel tile), one partial per partition
+    c = q.make_config(0, 4, 128, 128, 4, 1)
+    nbytes = q.qlin_workspace_bytes(FP8, 300, 512, 2048, c)
+    counters = -(-(3 * 4 * 4) // 256) * 256
+    assert nbytes == counters + -(-(4 * 300 * 512 * 4) // 256) * 256
+    assert q.qlin_workspace_bytes(FP8, 300, 512, 2048, q.make_config(0, 1, 128, 128, 4, 1)) == 0
+
+
 def test_split_k_workspace_is_checked_before_launch():
     c = q.make_config(swap_ab=1, split_k=4, tile_m=16, tile_n=32, waves=4, k_waves=4)
     need = q.qlin_workspace_bytes(FP8, 4, 256, 2048, c)

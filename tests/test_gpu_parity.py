@@ -46,6 +46,9 @@ SCHEDULES = {
     "nw4": cfg(0, 3, 16, 128, 8, 2),
     "nr4": cfg(1, 2, 32, 64, 1, 1),
     "w8k8": cfg(0, 1, 16, 16, 8, 8),
+    # the large-M kernel: 64- or 128-token tiles of 128 channels, 4 waves
+    "big64": cfg(0, 1, 64, 128, 4, 1),
+    "big128_split3": cfg(0, 3, 128, 128, 4, 1),
 }
 # the same with packed-atomic reduction (exact formats only)
 PACKED = {
@@ -188,7 +191,7 @@ def test_linear_fused_ragged_k(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 def test_linear_selected_schedule(fmt):
-    for M in (1, 4, 24):
+    for M in (1, 4, 24, 200):
         N, K = 512, 2048
         x = wl.activations(fmt, N, K, M)
         w = wl.random_weights(N, K, 80 + M)
@@ -212,7 +215,7 @@ def test_ragged_k(fmt, K):
     M, N = 5, 256
     x = wl.random_bf16((M, K), K)
     w = wl.random_weights(N, K, K + 1)
-    for sched in ("std", "swap", "splitk2", "splitk16", "nw4"):
+    for sched in ("std", "swap", "splitk2", "splitk16", "nw4", "big64", "big128_split3"):
         check_linear(fmt, M, N, K, x, w, sched, "ragged K")
 
 
@@ -360,3 +363,16 @@ def test_zero_tokens_is_a_no_op():
     assert q.qlin_quantize_act(fmt, 0, 512, y, 512, xq, xs) == 0
     torch.cuda.synchronize()
     assert int((y == 7).sum()) == 256
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("M", [63, 64, 129, 200])
+def test_large_m_kernel(fmt, M):
+    """The large-M kernel across token-tile tails, a channel tail (N = 384 +
+    128 for the block format, 3 or 4 tiles of 128) and split-K."""
+    N, K = (512 if fmt == wl.BLOCK_FP8 else 400), 1536
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 120 + M)
+    for c in (cfg(0, 1, 64, 128, 4, 1), cfg(0, 1, 128, 128, 4, 1), cfg(0, 4, 128, 128, 4, 1),
+              cfg(0, 2, 64, 128, 4, 1)):
+        check_linear(fmt, M, N, K, x, w, c, "large M")
