@@ -67,10 +67,33 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 template <int FMT>
 __device__ __forceinline__ float qmax_of() { return FMT == FMT_I8 ? 127.0f : 448.0f; }
 
+// Cross-lane maxima through DPP lane permutations (operand modifiers of
+// ordinary vector instructions on gfx9-family targets: no LDS traffic).
+// Each step takes the maximum with a permuted copy; lanes a step does not
+// write keep their own value.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float max_dpp(float v) {
+    const int moved = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return fmaxf(v, __int_as_float(moved));
+}
+
+// maximum over each row of 16 lanes, in every lane of the row:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+__device__ __forceinline__ float row16_max(float v) {
+    v = max_dpp<0xB1>(v);
+    v = max_dpp<0x4E>(v);
+    v = max_dpp<0x141>(v);
+    return max_dpp<0x140>(v);
+}
+
+// maximum over the wave (uniform): the row maxima are folded into the last
+// row by row_bcast:15 (rows 1 and 3) and row_bcast:31 (rows 2 and 3), and
+// read from lane 63
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = row16_max(v);
+    v = max_dpp<0x142, 0xA>(v);
+    v = max_dpp<0x143, 0xC>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // --------------------------------------------------- activation quantization

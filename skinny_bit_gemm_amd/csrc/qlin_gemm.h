@@ -361,9 +361,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 int row = row0, c = c0;
 #pragma unroll
                 for (int i = 0; i < XC; ++i) {
-                    float amax = absmax8(xr[i]);
-#pragma unroll
-                    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+                    const float amax = row16_max(absmax8(xr[i]));
                     const float sc = amax == 0.0f ? 0.0f : amax / 448.0f;
                     if (row < R) {
                         stage8(row, c_lo + c, quant8<FMT>(xr[i], sc, recip_scale(sc)));

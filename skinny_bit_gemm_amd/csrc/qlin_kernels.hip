@@ -77,9 +77,7 @@ __global__ __launch_bounds__(256) void quant_group_kernel(const uint16_t *__rest
     const int g = live ? gi - m * G : 0;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (live) v = *reinterpret_cast<const uint4 *>(x + (int64_t)m * ldx + g * kGroup + j * 8);
-    float amax = absmax8(v);
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const float amax = row16_max(absmax8(v));
     const float s = amax == 0.0f ? 0.0f : amax / 448.0f;
     if (!live) return;
     if (j == 0) xs[(int64_t)m * G + g] = s;

@@ -69,7 +69,7 @@ def candidates(fmt, M, N, K):
     if M > 32:
         # the large-M kernel: 64- / 128-token tiles of 128 channels
         for tmb in (64, 128):
-            for split in (1, 2, 3, 4, 6, 8):
+            for split in (1, 2, 3, 4, 6, 8, 12, 16):
                 kbs = -(-nkb // split)
                 eff = -(-nkb // kbs)
                 c = q.make_config(0, eff, tmb, 128, 4, 1, 0, 0)
