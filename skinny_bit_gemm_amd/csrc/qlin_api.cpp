@@ -48,6 +48,9 @@ qlin_status resolve_config(qlin_format fmt, int M, int N, int K, const qlin_conf
     if (st != QLIN_OK) return st;
     if (found) return QLIN_OK;
     if (strict_mode()) return QLIN_ERR_NO_CONFIG;
+    st = table_nearest(fmt, M, N, K, out, &found);
+    if (st != QLIN_OK) return st;
+    if (found) return QLIN_OK;
     default_config(fmt, M, N, K, out);
     return QLIN_OK;
 }

@@ -61,6 +61,7 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
 
 // Host-side selection table (qlin_table.cpp).
 qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out, bool *found);
+qlin_status table_nearest(qlin_format fmt, int M, int N, int K, qlin_config *out, bool *found);
 void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out);
 int token_bucket(int M);
 bool strict_mode();

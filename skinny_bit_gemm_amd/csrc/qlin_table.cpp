@@ -18,6 +18,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -152,13 +153,51 @@ qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out,
     return QLIN_OK;
 }
 
-// Built-in rule for shapes without a table entry (permissive mode).  It
-// follows the pages' example heuristic of dispatching to Swap-AB below 32
-// tokens (section "Kernel Implementation") and chooses a split so that the
-// grid has about four workgroups per compute unit, with at least one K block
-// per wave; small token counts quantize inside the GEMM (where the tile's
-// rows fit its registers) and combine exact partitions with packed atomics.
-// From 128 tokens on it takes the large-M kernel (64-token tiles).
+// Configuration of the tuned shape nearest to (N, K) in the same token
+// bucket, for shapes the table does not list (permissive mode).  Distance is
+// |log2 N/N'| + |log2 K/K'|, plus 1/2 for an entry of another per-token
+// format (the fp8 and int8 schedules stream the same bytes) and 1 between
+// the per-token and the block-scaled formats.  An entry whose configuration
+// does not fit the shape is passed over (a fused one first drops the fused
+// quantization).
+qlin_status table_nearest(qlin_format fmt, int M, int N, int K, qlin_config *out, bool *found) {
+    TableState &s = state();
+    std::lock_guard<std::mutex> lk(s.mu);
+    ensure_loaded(s);
+    *found = false;
+    const int b = token_bucket(M);
+    if (b < 0) return QLIN_OK;
+    double best = 1e30;
+    for (const auto &e : s.entries) {
+        const int efmt = std::get<0>(e.first), eN = std::get<1>(e.first), eK = std::get<2>(e.first);
+        if (std::get<3>(e.first) != b) continue;
+        double d = fabs(log2((double)N / eN)) + fabs(log2((double)K / eK));
+        if (efmt != (int)fmt) d += (efmt == QLIN_BLOCK_FP8) != (fmt == QLIN_BLOCK_FP8) ? 1.0 : 0.5;
+        if (d >= best) continue;
+        qlin_config c = e.second;
+        Plan p;
+        if (make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) {
+            if (!c.fuse_quant) continue;
+            c.fuse_quant = 0;
+            if (make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) continue;
+        }
+        best = d;
+        *out = c;
+        *found = true;
+    }
+    return QLIN_OK;
+}
+
+// Built-in rule for shapes with no usable table entry (permissive mode, an
+// empty table or more than 512 tokens).  Up to 64 tokens: 64-column tiles of
+// four waves, each K block range shared by two waves, and the smallest
+// power-of-two split that gives at least 192 workgroups (about three
+// quarters of a workgroup per compute unit) while each wave keeps at least
+// one K block; splits of four and more go through Swap-AB.  This is the
+// pick that measured closest to the best forced schedule over the 8B-class
+// shapes of all three formats.  Up to four tokens quantize inside the GEMM
+// where the rows fit.  From 128 tokens on it takes the large-M kernel
+// (64-token tiles).
 void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
     qlin_config c;
     if (M >= 128) {
@@ -168,20 +207,19 @@ void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
         return;
     }
     c.tile_m = M <= 16 ? 16 : 32;
-    c.swap_ab = M < 32 ? 1 : 0;
     c.waves = 4;
-    c.k_waves = 4;
-    c.tile_n = N % 32 == 0 ? 32 : 16;
+    c.k_waves = 2;
+    c.tile_n = 64;
     const int n_tiles = (N + c.tile_n - 1) / c.tile_n;
     const int m_tiles = (M + c.tile_m - 1) / c.tile_m;
     const int nkb = (K + kGroup - 1) / kGroup;
     int split = 1;
-    while (split < kMaxSplit && (int64_t)n_tiles * m_tiles * split < 1024 &&
+    while (split < kMaxSplit && (int64_t)n_tiles * m_tiles * split < 192 &&
            nkb / (split * 2) >= c.k_waves)
         split *= 2;
     c.split_k = split;
-    const bool exact = fmt == QLIN_W8A8_INT8 || (fmt == QLIN_FP8_DYNAMIC && K <= 40960);
-    c.reduce = exact && M <= 8 ? 1 : 0;
+    c.swap_ab = split >= 4 ? 1 : 0;
+    c.reduce = 0;
     c.fuse_quant = M <= 4 && c.tile_m == 16 ? 1 : 0;
     Plan p;
     if (c.fuse_quant && make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) c.fuse_quant = 0;

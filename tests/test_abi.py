@@ -151,15 +151,13 @@ def test_zero_tokens_gemm_is_ok_without_launch():
     assert gemm(M=0) == OK
 
 
-def test_token_bucket_rounding_and_default_rule():
-    # no entry for this odd shape: permissive mode answers with the built-in rule
-    c = q.qlin_select_variant(FP8, 3, 1024, 1024)
-    assert c.tile_m == 16 and c.swap_ab == 1
-    c32 = q.qlin_select_variant(FP8, 32, 1024, 1024)
-    assert c32.tile_m == 32 and c32.swap_ab == 0
+def test_any_shape_gets_a_valid_config():
+    # listed or not, every token count (also beyond the largest bucket) gets
+    # a configuration that fits the shape
     for M in (1, 5, 31, 100, 600):
-        c = q.qlin_select_variant(I8, M, 2048, 4096)
-        assert q.qlin_validate_config(I8, M, 2048, 4096, c) == OK
+        for fmt, N, K in ((I8, 2048, 4096), (FP8, 1008, 1040), (BLK, 384, 640)):
+            c = q.qlin_select_variant(fmt, M, N, K)
+            assert q.qlin_validate_config(fmt, M, N, K, c) == OK
 
 
 def write_table(tmp_path, body, header="qlin-table 1 gfx950"):
@@ -178,6 +176,51 @@ def test_table_load_lookup_and_bucket_round_up(tmp_path):
     assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves) == (1, 2, 16, 64, 4, 2)
     c = q.qlin_select_variant(FP8, 25, 1024, 1024)          # 25 -> bucket 32
     assert (c.swap_ab, c.split_k, c.tile_m) == (0, 4, 32)
+
+
+def test_default_rule_without_table_entries(tmp_path):
+    # an empty table: the built-in rule.  N = K = 1024: 16 tiles of 64
+    # columns; the split doubles while the grid is under 192 workgroups and
+    # each of the two K waves keeps a block: 8 K blocks -> split 4 (Swap-AB)
+    assert q.qlin_load_table(write_table(tmp_path, "")) == OK
+    assert q.qlin_table_entries() == 0
+    c = q.qlin_select_variant(FP8, 3, 1024, 1024)
+    assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves, c.reduce) == (1, 4, 16, 64, 4, 2, 0)
+    assert c.fuse_quant == 1                      # 3 rows of 1024 values fit the registers
+    c = q.qlin_select_variant(FP8, 32, 1024, 1024)
+    assert (c.split_k, c.tile_m, c.fuse_quant) == (4, 32, 0)
+    c = q.qlin_select_variant(I8, 4, 12288, 4096)  # 192 tiles already: no split
+    assert (c.swap_ab, c.split_k) == (0, 1)
+    c = q.qlin_select_variant(I8, 200, 4096, 4096)
+    assert (c.tile_m, c.tile_n, c.k_waves) == (64, 128, 1)
+
+
+def test_nearest_entry_for_unlisted_shapes(tmp_path):
+    path = write_table(tmp_path,
+                       "fp8_dynamic 2048 2048 4 0 2 16 32 4 2 1 0\n"
+                       "w8a8_int8 1024 1024 4 1 1 16 64 8 4 0 1\n"
+                       "fp8_dynamic 1024 1024 8 1 2 16 64 4 2 0 0\n")
+    assert q.qlin_load_table(path) == OK
+    # same bucket only; a per-token format at distance 0 + 1/2 beats the same
+    # format at distance 2
+    c = q.qlin_select_variant(FP8, 3, 1024, 1024)
+    assert (c.swap_ab, c.split_k, c.tile_n, c.waves, c.k_waves, c.fuse_quant) == (1, 1, 64, 8, 4, 1)
+    # nearer in N and K wins within the format
+    c = q.qlin_select_variant(FP8, 4, 2048, 4096)
+    assert (c.split_k, c.tile_n, c.reduce) == (2, 32, 1)
+    # the block format counts a per-token entry at distance + 1; the packed
+    # reduction is for exact formats only, so (2048, 2048) is passed over
+    c = q.qlin_select_variant(BLK, 4, 2048, 2048)
+    assert (c.split_k, c.tile_n, c.waves) == (1, 64, 8)
+    # a fused entry whose rows do not fit the registers at this K loses the
+    # fused quantization, not the rest
+    c = q.qlin_select_variant(I8, 4, 1024, 65536)
+    assert (c.swap_ab, c.tile_n, c.waves, c.k_waves, c.fuse_quant) == (1, 64, 8, 4, 0)
+    # another bucket: its own entry, or the built-in rule when it has none
+    c = q.qlin_select_variant(FP8, 8, 4096, 4096)
+    assert (c.swap_ab, c.split_k, c.tile_n) == (1, 2, 64)
+    c = q.qlin_select_variant(FP8, 16, 1024, 1024)
+    assert (c.split_k, c.k_waves) == (4, 2)
 
 
 def test_strict_mode_missing_entry_is_an_error(tmp_path):
