@@ -128,11 +128,11 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     p->kb_per_split = (p->nkb + c.split_k - 1) / c.split_k;
     p->nsplit = (p->nkb + p->kb_per_split - 1) / p->kb_per_split;
     // activation codes of the tile's existing token rows (128 bytes per row
-    // and K block) plus, for the block format, one fp32 scale per row and block
+    // and K block, and one more 16-byte slot per row, which makes the row
+    // stride odd) plus, for the block format, one fp32 scale per row and block
     const int rows = M < c.tile_m ? M : c.tile_m;
-    // (the staging gives each group of rows an odd number of 16-byte slots)
-    const int per_block = (rows | 1) * kGroup + (fmt == QLIN_BLOCK_FP8 ? rows * 4 : 0);
-    int pb = kLdsBudget / per_block;
+    const int per_block = rows * kGroup + (fmt == QLIN_BLOCK_FP8 ? rows * 4 : 0);
+    int pb = (kLdsBudget - rows * 16) / per_block;
     if (pb > p->kb_per_split) pb = p->kb_per_split;
     p->phase_blocks = pb;
     // In-kernel quantization: one phase (the workgroup's K range fits the
@@ -151,7 +151,7 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     }
     p->xc = xc;
     if (!gemm_variant_exists(fmt, c.tile_m, nr, xc)) return QLIN_ERR_INVALID_ARG;
-    size_t lds = (size_t)pb * per_block;
+    size_t lds = (size_t)pb * per_block + (size_t)rows * 16;
     const size_t red = (size_t)(c.k_waves - 1) * nw * nr * mt * 64 * 16;
     if (red > lds) lds = red;
     p->lds_bytes = lds;

@@ -41,24 +41,26 @@ namespace qlin {
 // in PF register slots, consumed and refilled in batches.
 //
 // Activations.  The workgroup's token rows for its K range are staged once
-// in LDS, only the rows that exist (R = min(TM, M - m0)), laid out as
-// [K block][half][quarter][row][16 bytes] with Rs = R | 1 row slots per
-// (block, half, quarter) group: the 16 lanes of a quarter read 16
-// consecutive 16-byte chunks, so the two ds_read_b128 per block are free of
-// bank conflicts, and the odd group stride spreads the staging writes (which
-// walk along K within a row, one group per 16 bytes) over the banks.  Lanes
-// whose row is past R use zeros.  When Rs x (K range) does not fit the LDS
+// in LDS, only the rows that exist (R = min(TM, M - m0)), row by row: row r
+// of the phase's K range starts at 16-byte slot r * RS, RS = 8 P + 1 for at
+// most P K blocks per phase.  The odd row stride puts the 16 rows that the
+// 16 lanes of a quarter read at 16 different bank groups, so the two
+// ds_read_b128 per block are free of bank conflicts, and a row's K range is
+// contiguous, as in memory.  Lanes
+// whose row is past R use zeros.  When R x RS slots do not fit the LDS
 // budget the range is processed in phases.
 //
 // Order of the memory requests.  The vector memory counter a wave waits on
 // counts requests in issue order, so a wait for one load is a wait for every
 // older one.  Each phase therefore first requests its activations (codes,
-// or bf16 values to quantize), then the first PF weight blocks, then the
-// epilogue's scales; the activations arrive first (they are few and
-// L2-resident) and are staged in LDS while the weights are still in
-// flight.  Every weight slot is requested on every path (a slot past the
-// wave's last block uses an out-of-range offset, which returns zeros without
-// touching memory), so the compiler's waits count exactly.
+// or bf16 values to quantize), then the epilogue's scales, then the first PF
+// weight blocks; the activations arrive first (they are few and
+// L2-resident) and are staged in LDS while the weights are still in flight.
+// Codes are copied by the memory system itself into LDS (loads with the LDS
+// bit, no registers); bf16 values come through registers and are quantized
+// on the way.  Every weight slot is requested on every path (a slot past
+// the wave's last block uses an out-of-range offset, which returns zeros
+// without touching memory), so the waits count exactly.
 //
 // Standard: A = activations (tokens are the MFMA rows), B = weights.  The
 // 16x16 result lane l holds column l % 16 = channel and rows 4(l/16)+i =
@@ -165,16 +167,14 @@ __device__ __forceinline__ void wait_memory_idle() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// byte offset in the LDS staging layout [block][half][quarter][row][16B] of
-// 8-byte chunk cl (0, 1, ... along the K range) of row `row` (R rows)
-__device__ __forceinline__ int stage_offset8(int cl, int row, int Rs) {
-    const int b = cl >> 4, cc = cl & 15, u = cc >> 1;
-    return (((b * 2 + (u & 1)) * 4 + (u >> 1)) * Rs + row) * 16 + (cc & 1) * 8;
-}
+// byte offset in the LDS staging layout (row stride RS 16-byte slots) of
+// 8-byte chunk cl (0, 1, ... along the K range) of row `row`
+__device__ __forceinline__ int stage_offset8(int cl, int row, int RS) { return row * RS * 16 + cl * 8; }
 
-// activation 16-byte units staged per thread straight from registers (the
-// rest, for very large tiles, in a loop afterwards)
-constexpr int kStageRegs = 4;
+// s_waitcnt operand that waits until at most n vector memory requests are
+// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int FMT, bool SWAP, int MT, int NR, int PF, int XC>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     const int r16 = lane & 15, quarter = lane >> 4;
     const int G = (K + kGroup - 1) / kGroup;
     const int R = min(16 * MT, M - m0);   // token rows that exist in this tile
-    const int Rs = R | 1;                  // row groups of the LDS staging, an odd number of rows
+    const int RS = 8 * g.phase_blocks + 1;   // LDS staging row stride in 16-byte slots (odd)
     // fused path: the first column of workgroups also stores the codes and
     // scales it produces (every workgroup of a row of tiles produces the same)
     const bool writer = FUSE && blockIdx.x == 0;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     // (rows past R read an existing row, and their data is replaced by zeros)
     int lds_lo[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) lds_lo[mt] = (quarter * Rs + (mt * 16 + r16 < R ? mt * 16 + r16 : 0)) * 16;
+    for (int mt = 0; mt < MT; ++mt) lds_lo[mt] = ((mt * 16 + r16 < R ? mt * 16 + r16 : 0) * RS + 2 * quarter) * 16;
 
     acc_t acc[NR][MT];
 #pragma unroll
@@ -263,13 +263,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     // request K block kb into a register slot (the block format also fetches
     // each sub-tile's 128x128 weight-block scale); a dead slot (live false)
     // is requested with out-of-range offsets
+    // (the block scales come by buffer loads too, so that they count in the
+    // same vector memory counter as the weights)
+    const __amdgpu_buffer_rsrc_t bsr = buffer_rsrc(g.wsc, FMT == FMT_BLOCK ? (uint32_t)(N / kGroup * G * 4) : 0u);
     auto issue = [&](v8i(&slot)[NR], float(&sws)[NR], int kb, bool live) {
         const int k = kb * kGroup;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             slot[r] = load_w(wrs[r], lane_off, kb, k + quarter * 32, K, live);
-            if constexpr (FMT == FMT_BLOCK)
-                sws[r] = g.wsc[(int64_t)(min(nsub[r], N - 1) / kGroup) * G + min(kb, G - 1)];
+            if constexpr (FMT == FMT_BLOCK) {
+                const int soff = __builtin_amdgcn_readfirstlane(
+                    ((min(nsub[r], N - 1) / kGroup) * G + min(kb, G - 1)) * 4);
+                sws[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bsr, 0, soff, 0));
+            }
         }
     };
 
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         const int nblk = min(kb_end - pb0, g.phase_blocks);
         // this wave's blocks of the phase are kw, kw + kstep, ... (a uniform count)
         const int nmine = kw < nblk ? (nblk - kw + kstep - 1) / kstep : 0;
-        float *s_scale = reinterpret_cast<float *>(smem + (size_t)g.phase_blocks * kGroup * Rs);
+        float *s_scale = reinterpret_cast<float *>(smem + (size_t)R * RS * 16);
 
         // ---- 1. activation requests
         // fused: the tile's R rows x cn chunk positions of 8 values (per-token
@@ -300,12 +306,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             if (c >= cn) { c -= cn; ++row; }
         };
         uint4 xr[FUSE ? XC : 1];
-        // unfused: the first kStageRegs 16-byte units of codes per thread
-        // (and, block format, one activation scale)
-        const int items = R * nblk * 8;
-        uint4 sv[FUSE ? 1 : kStageRegs];
-        int spos[FUSE ? 1 : kStageRegs];   // LDS byte position of each, or -1
-        float sx = 0.0f;
+        if (pb0 != kb_begin) __syncthreads();   // the previous phase's readers are done
+        // nothing is in flight here (the previous phase's dead weight slots
+        // are done by now; this tells the compiler so)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
         if constexpr (FUSE) {
             const __amdgpu_buffer_rsrc_t xrs =
                 buffer_rsrc(g.x + (int64_t)m0 * g.ldx, (uint32_t)(((R - 1) * g.ldx + K) * 2));
@@ -317,22 +321,50 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 next_slot(row, c);
             }
         } else {
+            // the codes go from memory straight into the LDS staging layout:
+            // a 16-byte buffer load with the LDS bit writes lane l's data 16 l
+            // bytes past the wave's LDS address, so one request copies 64
+            // consecutive 16-byte chunks of a row (8 K blocks): the lane
+            // offset is 16 l and the row and chunk group are scalars.  The
+            // waves take the R x ceil(nblk / 8) requests in turn; lanes past
+            // the phase's blocks are masked off, chunks past K are read out of
+            // range, which stores zeros.
             const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(g.xq + (int64_t)m0 * K, (uint32_t)(R * K));
-#pragma unroll
-            for (int s = 0; s < kStageRegs; ++s) {
-                const int it = threadIdx.x + s * nthreads;
-                const int c = it & 7, rest = it >> 3;
-                const int b = rest % nblk, row = rest / nblk;
-                const int k = (pb0 + b) * kGroup + c * 16;
-                sv[s] = load16(qrs, it < items && k < K ? (uint32_t)(row * K + k) : kOutOfRange);
-                spos[s] = it < items ? (((b * 2 + (c & 1)) * 4 + (c >> 1)) * Rs + row) * 16 : -1;
+            const int ngrp = (nblk + 7) >> 3;        // 64-chunk groups per row
+            const int nreq = R * ngrp;
+            const int dr = nwaves / ngrp, di = nwaves - dr * ngrp;
+            int r = wave / ngrp, i = wave - r * ngrp;   // this wave's first request
+            for (int t = wave; t < nreq; t += nwaves) {
+                const int c0 = pb0 * 8 + i * 64;                    // first chunk (absolute)
+                const int live = min(64, nblk * 8 - i * 64);        // chunks of the phase
+                const int inK = (K >> 4) - c0;                      // chunks before K
+                if (lane < live)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        qrs, (__attribute__((address_space(3))) void *)(smem + (r * RS + i * 64) * 16), 16,
+                        lane < inK ? (uint32_t)lane * 16 : kOutOfRange,
+                        __builtin_amdgcn_readfirstlane(r * K + c0 * 16), 0, 0);
+                r += dr;
+                i += di;
+                if (i >= ngrp) { i -= ngrp; ++r; }
             }
             if constexpr (FMT == FMT_BLOCK) {
+                // the activation scales of the phase, [block][row] after the
+                // codes, the same way with 4-byte loads (lane l writes 4 l
+                // bytes past the wave's address)
                 const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(g.xs + (int64_t)m0 * G, (uint32_t)(R * G * 4));
-                const int it = threadIdx.x;
-                const int row = it % R, b = it / R;
-                const uint32_t off = it < nblk * R ? (uint32_t)((row * G + pb0 + b) * 4) : kOutOfRange;
-                sx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+                const int nsc = nblk * R;
+                const int sl0 = wave * 64 + lane;
+                int sb = sl0 / R, sr = sl0 - sb * R;
+                const int dsb = nthreads / R, dsr = nthreads - dsb * R;
+                for (int s0 = wave * 64; s0 < nsc; s0 += nthreads) {
+                    if (s0 + lane < nsc)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            srs, (__attribute__((address_space(3))) void *)(s_scale + s0), 4,
+                            (uint32_t)((sr * G + pb0 + sb) * 4), 0, 0, 0);
+                    sr += dsr;
+                    sb += dsb;
+                    if (sr >= R) { sr -= R; ++sb; }
+                }
             }
         }
 
@@ -347,11 +379,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- 3. activations into LDS
-        if (pb0 != kb_begin) __syncthreads();   // the previous phase's readers are done
         if constexpr (FUSE) {
             const int kc0 = kb_begin * 16, kc1 = kb_end * 16;   // chunks staged (absolute)
             auto stage8 = [&](int row, int c, uint2 codes) {   // c absolute
-                *reinterpret_cast<uint2 *>(smem + stage_offset8(c - kc0, row, Rs)) = codes;
+                *reinterpret_cast<uint2 *>(smem + stage_offset8(c - kc0, row, RS)) = codes;
                 if (writer && c < nchunk)
                     *reinterpret_cast<uint2 *>(g.xq_out + (int64_t)(m0 + row) * K + c * 8) = codes;
             };
@@ -410,29 +441,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 }
             }
         } else {
-            auto put = [&](int it, uint4 v) {
-                const int c = it & 7, rest = it >> 3;
-                const int b = rest % nblk, row = rest / nblk;
-                *reinterpret_cast<uint4 *>(smem + (((b * 2 + (c & 1)) * 4 + (c >> 1)) * Rs + row) * 16) = v;
-            };
-#pragma unroll
-            for (int s = 0; s < kStageRegs; ++s)
-                if (spos[s] >= 0) *reinterpret_cast<uint4 *>(smem + spos[s]) = sv[s];
-            for (int it = threadIdx.x + kStageRegs * nthreads; it < items; it += nthreads) {
-                const int c = it & 7, rest = it >> 3;
-                const int b = rest % nblk, row = rest / nblk;
-                const int k = (pb0 + b) * kGroup + c * 16;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (k < K) v = *reinterpret_cast<const uint4 *>(g.xq + (int64_t)(m0 + row) * K + k);
-                put(it, v);
-            }
-            if constexpr (FMT == FMT_BLOCK) {
-                if ((int)threadIdx.x < nblk * R) s_scale[threadIdx.x] = sx;   // [block][row]
-                for (int it = threadIdx.x + nthreads; it < nblk * R; it += nthreads) {
-                    const int row = it % R, b = it / R;
-                    s_scale[it] = g.xs[(int64_t)(m0 + row) * G + pb0 + b];
-                }
-            }
+            // this thread's staging loads are done once at most the younger
+            // requests (the first batch of weight slots: two loads per
+            // sub-tile and slot, and the block format's block scale) are
+            // outstanding; the barrier below then makes every wave's slots
+            // visible
+            constexpr int younger = PF * NR * (FMT == FMT_BLOCK ? 3 : 2);
+            static_assert(younger < 64, "vmcnt holds at most 63");
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(younger));
         }
         __syncthreads();
 
@@ -443,13 +459,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             const int b = kw + jb * kstep;
             // activation fragments of this block (zeros past row R; the read
             // address is clamped to an existing row)
-            const int boff = __builtin_amdgcn_readfirstlane(b * 8 * Rs * 16);   // uniform
+            const int boff = b * kGroup;   // uniform
             v8i xf[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const bool live = mt * 16 + r16 < R;
                 const uint4 lo = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + boff);
-                const uint4 hi = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + 4 * Rs * 16 + boff);
+                const uint4 hi = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + 16 + boff);
                 xf[mt] = join(select4(live, lo), select4(live, hi));
             }
             if constexpr (FMT == FMT_BLOCK) {

@@ -180,6 +180,20 @@ def test_linear_fused_packed_stride_and_phases(fmt):
     assert q.qlin_validate_config(fmt, 16, N, K, cfg(1, 1, 16, 64, 8, 2, fuse=1)) == q.QLIN_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_staging_phases_ragged(fmt):
+    """Activation staging over several LDS phases with a shorter last phase,
+    ragged token rows (29 of a 32-row tile) and, for the per-token formats,
+    a partial last K block: 29 rows x 65 K blocks take phases of 21, 21, 21
+    and 2 blocks, each row copied in requests of up to 8 blocks."""
+    M, N = 29, 256
+    K = 8320 if fmt == wl.BLOCK_FP8 else 8240
+    x = wl.activations(fmt, N, K, M) if K % 128 == 0 else wl.random_bf16((M, K), 17)
+    w = wl.random_weights(N, K, 18)
+    for c in (cfg(1, 1, 32, 32, 4, 2), cfg(0, 2, 32, 64, 8, 2)):
+        check_layer(fmt, M, N, K, x, w, c)
+
+
 @pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
 def test_linear_fused_ragged_k(fmt):
     M, N, K = 5, 256, 1040
