@@ -13,14 +13,19 @@
 // output (tokens x channels) and a range of 128-wide K blocks; the waves
 // form a 2 x 2 grid, each computing (BM/2) x 64 with 16x16x128 fp8 (or
 // 16x16x64 int8) matrix-core instructions on the same lane -> (row, k)
-// fragment assignment as the skinny kernel.  Both operand tiles of a K block
-// go through LDS (double buffered, one barrier per block), each as
-// [half][quarter][row][16 bytes] with an odd number of row slots per group:
-// the fragment reads (16 lanes on 16 consecutive rows) and the staging writes
-// (8 lanes on the 8 groups of one row) are free of bank conflicts.  The
-// tiles are requested from memory STAGES blocks ahead into registers (every
-// request issued on every path, past-the-end ones with out-of-range
-// offsets, so the waits count exactly).
+// fragment assignment as the skinny kernel.
+//
+// Operand staging.  Both tiles of a K block are copied by the memory system
+// straight into LDS (buffer loads with the LDS bit: lane l's 16 bytes land
+// 16 l bytes past the wave's LDS address), through a ring of STAGES buffers,
+// STAGES - 1 blocks ahead of the computation, with one barrier per block.
+// A tile is stored row by row, 128 bytes per row, 16-byte chunk c of row r
+// at position c ^ (r & 7): one request copies 8 whole rows (1 KB) with a
+// per-lane offset that never changes, and the fragment reads (8 lanes of a
+// pass on 8 consecutive rows, same chunk) hit 8 different bank groups.  No
+// register holds staged data.  Every request is issued on every path
+// (past-the-end ones out of range, which store zeros), so each wave has the
+// same number of requests per block and an explicit wait counts exactly.
 //
 // Tile order.  The grid is one-dimensional and the hardware deals workgroups
 // to the 8 XCDs round robin; tiles are numbered so that the M tiles sharing
@@ -41,22 +46,92 @@ struct BigTile {
     static constexpr int WM = BM / 2;        // rows per wave
     static constexpr int FM = WM / 16;       // 16-row fragments per wave
     static constexpr int FN = 4;             // 16-channel fragments per wave (64 channels)
-    static constexpr int PA = BM + 1;        // row slots per LDS group, odd
-    static constexpr int PB = kBigN + 1;
-    static constexpr int UA = BM * 8 / kBigThreads;      // 16-byte units per thread per block
-    static constexpr int UB = kBigN * 8 / kBigThreads;
-    static constexpr int STAGES = 3;                     // blocks requested ahead
-    static constexpr int A_BYTES = 8 * PA * 16;
-    static constexpr int B_BYTES = 8 * PB * 16;
-    static constexpr int BUF_BYTES = A_BYTES + B_BYTES + (FMT == FMT_BLOCK ? BM * 4 : 0);
+    // LDS buffers (blocks in flight: STAGES - 1), sized so that two
+    // workgroups share a compute unit: one computes while the other waits
+    static constexpr int STAGES = BM == 64 ? 3 : 2;
+    static constexpr int WG_PER_CU = 2;
+    static constexpr int A_BYTES = BM * kGroup;
+    static constexpr int B_BYTES = kBigN * kGroup;
+    // block format: token scales of the block (one 64-entry group per wave,
+    // entries past BM zero) and the weight block's scale
+    static constexpr int S_BYTES = FMT == FMT_BLOCK ? 4 * 64 * 4 + 16 : 0;
+    static constexpr int BUF_BYTES = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int REQ_A = BM / 8 / 4;   // 8-row requests per wave and block
+    static constexpr int REQ_B = kBigN / 8 / 4;
+    static constexpr int REQ = REQ_A + REQ_B + (FMT == FMT_BLOCK ? 2 : 0);
+    static_assert((STAGES - 2) * REQ < 64, "vmcnt holds at most 63");
+    static_assert(STAGES * BUF_BYTES * WG_PER_CU <= 160 * 1024, "LDS of a compute unit");
 };
 
+// Fragment reads from LDS, as inline-assembly blocks that end with their
+// own wait.  (Written as plain loads, the compiler would make every LDS
+// read wait for all the LDS copies in flight, the later blocks' included,
+// which would drain the ring every block.)  A fragment is two 16-byte
+// halves at the lane's lo / hi chunk addresses; the 4 channel fragments of
+// a wave are 2048 bytes (16 rows) apart.
+#define QLIN_RD(d, a, off) "ds_read_b128 %[" #d "], %[" #a "] offset:" #off "\n"
+#define QLIN_RD_B                                                                              \
+    QLIN_RD(b0l, bl, 0) QLIN_RD(b0h, bh, 0) QLIN_RD(b1l, bl, 2048) QLIN_RD(b1h, bh, 2048)      \
+        QLIN_RD(b2l, bl, 4096) QLIN_RD(b2h, bh, 4096) QLIN_RD(b3l, bl, 6144) QLIN_RD(b3h, bh, 6144)
+#define QLIN_OUT_B                                                                                \
+    [b0l] "=&v"(b[0][0]), [b0h] "=&v"(b[0][1]), [b1l] "=&v"(b[1][0]), [b1h] "=&v"(b[1][1]),      \
+        [b2l] "=&v"(b[2][0]), [b2h] "=&v"(b[2][1]), [b3l] "=&v"(b[3][0]), [b3h] "=&v"(b[3][1])
+
+// the wave's 4 channel fragments and its first token fragment
+__device__ __forceinline__ void lds_frags_first(v4i (&a)[2], v4i (&b)[4][2], uint32_t al, uint32_t ah,
+                                                uint32_t bl, uint32_t bh) {
+    asm volatile(QLIN_RD_B QLIN_RD(a0l, al, 0) QLIN_RD(a0h, ah, 0) "s_waitcnt lgkmcnt(0)"
+                 : QLIN_OUT_B, [a0l] "=&v"(a[0]), [a0h] "=&v"(a[1])
+                 : [bl] "v"(bl), [bh] "v"(bh), [al] "v"(al), [ah] "v"(ah)
+                 : "memory");
+}
+
+// block format: the same, plus the lane's 4 token scales of each of FM
+// token fragments (64 bytes, 16 rows, apart) and the weight block's scale
+template <int FM>
+__device__ __forceinline__ void lds_frags_first_scaled(v4i (&a)[2], v4i (&b)[4][2], v4i (&sa)[FM], float &sw,
+                                                       uint32_t al, uint32_t ah, uint32_t bl, uint32_t bh,
+                                                       uint32_t sl, uint32_t sb) {
+    static_assert(FM == 2 || FM == 4, "2 or 4 token fragments");
+    if constexpr (FM == 2)
+        asm volatile(QLIN_RD_B QLIN_RD(a0l, al, 0) QLIN_RD(a0h, ah, 0) QLIN_RD(s0, sl, 0) QLIN_RD(s1, sl, 64)
+                     "ds_read_b32 %[sw], %[sb]\n"
+                     "s_waitcnt lgkmcnt(0)"
+                     : QLIN_OUT_B, [a0l] "=&v"(a[0]), [a0h] "=&v"(a[1]), [s0] "=&v"(sa[0]), [s1] "=&v"(sa[1]),
+                       [sw] "=&v"(sw)
+                     : [bl] "v"(bl), [bh] "v"(bh), [al] "v"(al), [ah] "v"(ah), [sl] "v"(sl), [sb] "v"(sb)
+                     : "memory");
+    else
+        asm volatile(QLIN_RD_B QLIN_RD(a0l, al, 0) QLIN_RD(a0h, ah, 0) QLIN_RD(s0, sl, 0) QLIN_RD(s1, sl, 64)
+                         QLIN_RD(s2, sl, 128) QLIN_RD(s3, sl, 192) "ds_read_b32 %[sw], %[sb]\n"
+                     "s_waitcnt lgkmcnt(0)"
+                     : QLIN_OUT_B, [a0l] "=&v"(a[0]), [a0h] "=&v"(a[1]), [s0] "=&v"(sa[0]), [s1] "=&v"(sa[1]),
+                       [s2] "=&v"(sa[2]), [s3] "=&v"(sa[3]), [sw] "=&v"(sw)
+                     : [bl] "v"(bl), [bh] "v"(bh), [al] "v"(al), [ah] "v"(ah), [sl] "v"(sl), [sb] "v"(sb)
+                     : "memory");
+}
+
+// one more token fragment
+__device__ __forceinline__ void lds_frag(v4i (&a)[2], uint32_t al, uint32_t ah) {
+    asm volatile(QLIN_RD(a0l, al, 0) QLIN_RD(a0h, ah, 0) "s_waitcnt lgkmcnt(0)"
+                 : [a0l] "=&v"(a[0]), [a0h] "=&v"(a[1])
+                 : [al] "v"(al), [ah] "v"(ah)
+                 : "memory");
+}
+#undef QLIN_RD
+#undef QLIN_RD_B
+#undef QLIN_OUT_B
+
+__device__ __forceinline__ v8i join4(v4i lo, v4i hi) {
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 template <int FMT, int BM>
-__global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) {   // two per compute unit
     typedef BigTile<FMT, BM> T;
     typedef typename AccT<FMT>::type acc_t;
     typedef typename AccT<FMT>::scalar acc_s;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[T::STAGES * T::BUF_BYTES];
     __shared__ int s_last;
 
     const int M = g.M, N = g.N, K = g.K;
@@ -89,69 +164,48 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmLaunch g) {
     const __amdgpu_buffer_rsrc_t srs =
         buffer_rsrc(FMT == FMT_BLOCK ? (const void *)(g.xs + (int64_t)m0 * G) : (const void *)g.xs,
                     FMT == FMT_BLOCK ? (uint32_t)(rows_a * G * 4) : 0u);
-
-    // this thread's staging units: unit u = t + 256 i is (row u / 8, 16-byte
-    // chunk u % 8) of the block; its LDS slot and its offset in the tile
-    int a_lds[T::UA], b_lds[T::UB];
-    uint32_t a_off[T::UA], b_off[T::UB];
-    int a_k[T::UA], b_k[T::UB];
-#pragma unroll
-    for (int i = 0; i < T::UA; ++i) {
-        const int u = t + kBigThreads * i, row = u >> 3, c = u & 7;
-        a_lds[i] = (((c & 1) * 4 + (c >> 1)) * T::PA + row) * 16;
-        a_off[i] = (uint32_t)(row * K + c * 16);
-        a_k[i] = c * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < T::UB; ++i) {
-        const int u = t + kBigThreads * i, row = u >> 3, c = u & 7;
-        b_lds[i] = T::A_BYTES + (((c & 1) * 4 + (c >> 1)) * T::PB + row) * 16;
-        b_off[i] = (uint32_t)(row * K + c * 16);
-        b_k[i] = c * 16;
-    }
-
-    // register stages: the units of STAGES blocks in flight (block format:
-    // also the token scales of the block and the weight block's scale)
-    uint4 ra[T::STAGES][T::UA], rb[T::STAGES][T::UB];
-    float rs[T::STAGES], rw[T::STAGES];
     const __amdgpu_buffer_rsrc_t wrs =
         buffer_rsrc(g.wsc + (FMT == FMT_BLOCK ? (int64_t)(n0 / kGroup) * G : 0), FMT == FMT_BLOCK ? (uint32_t)(G * 4) : 0u);
-    auto request = [&](int st, int j) {   // block j of the range into stage st
+
+    // lane l of an 8-row request: row l / 8 of the request, LDS chunk
+    // position l % 8, which holds source chunk (l % 8) ^ (l / 8)
+    const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
+    const uint32_t lane_off = (uint32_t)(lrow * K + lchunk * 16);
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+
+    // requests of block j of the range into LDS buffer `buf`
+    // (buffers are addressed by their 32-bit LDS addresses)
+    auto issue = [&](int j, uint32_t base) {
         const bool live = j < nsteps;
         const int kb = kb_begin + j;
         const int k0 = kb * kGroup;
-        const int boff = __builtin_amdgcn_readfirstlane(k0);
+        const bool kin = live && k0 + lchunk * 16 < K;
 #pragma unroll
-        for (int i = 0; i < T::UA; ++i) {
-            const bool ok = live && k0 + a_k[i] < K;
-            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(ars, ok ? a_off[i] : kOutOfRange, boff, 0);
-            ra[st][i] = make_uint4(v[0], v[1], v[2], v[3]);
+        for (int i = 0; i < T::REQ_A; ++i) {
+            const int r0 = (wave * T::REQ_A + i) * 8;
+            const bool ok = kin && r0 + lrow < rows_a;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_ptr)(uintptr_t)(base + r0 * kGroup), 16,
+                                                     ok ? (uint32_t)(r0 * K) + lane_off : kOutOfRange,
+                                                     __builtin_amdgcn_readfirstlane(k0), 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < T::UB; ++i) {
-            const bool ok = live && k0 + b_k[i] < K;
-            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(brs, ok ? b_off[i] : kOutOfRange, boff, 0);
-            rb[st][i] = make_uint4(v[0], v[1], v[2], v[3]);
+        for (int i = 0; i < T::REQ_B; ++i) {
+            const int r0 = (wave * T::REQ_B + i) * 8;
+            const bool ok = kin && r0 + lrow < rows_b;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
+                                                     ok ? (uint32_t)(r0 * K) + lane_off : kOutOfRange,
+                                                     __builtin_amdgcn_readfirstlane(k0), 0, 0);
         }
         if constexpr (FMT == FMT_BLOCK) {
-            // token scales of the block (one per row, threads t < BM)
-            const bool ok = live && t < BM;
-            rs[st] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(srs, ok ? (uint32_t)((t * G + kb) * 4) : kOutOfRange, 0, 0));
-            rw[st] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(wrs, live ? (uint32_t)(kb * 4) : kOutOfRange, 0, 0));
-        }
-    };
-    float sw_now = 0.0f;                  // block format: weight block scale of the staged block
-    auto stage = [&](int st, int buf) {   // stage st -> LDS buffer buf
-        uint8_t *base = lds + buf * T::BUF_BYTES;
-        if constexpr (FMT == FMT_BLOCK) sw_now = rw[st];
-#pragma unroll
-        for (int i = 0; i < T::UA; ++i) *reinterpret_cast<uint4 *>(base + a_lds[i]) = ra[st][i];
-#pragma unroll
-        for (int i = 0; i < T::UB; ++i) *reinterpret_cast<uint4 *>(base + b_lds[i]) = rb[st][i];
-        if constexpr (FMT == FMT_BLOCK) {
-            if (t < BM) reinterpret_cast<float *>(base + T::A_BYTES + T::B_BYTES)[t] = rs[st];
+            const uint32_t sbase = base + T::A_BYTES + T::B_BYTES;
+            const int e = wave * 64 + lane;   // token row of this lane's scale
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                srs, (lds_ptr)(uintptr_t)(sbase + wave * 64 * 4), 4,
+                live && e < rows_a ? (uint32_t)((e * G + kb) * 4) : kOutOfRange, 0, 0, 0);
+            // the weight block's scale: lane 0 of every wave, to the same slot
+            if (lane == 0)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(uintptr_t)(sbase + 4 * 64 * 4), 4,
+                                                         live ? (uint32_t)(kb * 4) : kOutOfRange, 0, 0, 0);
         }
     };
 
@@ -161,30 +215,36 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmLaunch g) {
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
-    // the lane's fragment slots: row r16 of 16-row group f, quarter `quarter`
-    const int a_frag = (quarter * T::PA + wm * T::WM + r16) * 16;
-    const int b_frag = T::A_BYTES + (quarter * T::PB + wn * 64 + r16) * 16;
-    auto compute = [&](int buf) {
-        const uint8_t *base = lds + buf * T::BUF_BYTES;
+    // the lane's fragment: row (16-row group base + r16), chunks 2 quarter
+    // and 2 quarter + 1, at positions chunk ^ (row & 7); LDS byte addresses
+    const int a_row = wm * T::WM + r16, b_row = wn * 64 + r16;
+    const int sw = r16 & 7;   // row & 7 (group bases are multiples of 16)
+    const uint32_t c_lo = ((2 * quarter) ^ sw) * 16, c_hi = ((2 * quarter + 1) ^ sw) * 16;
+    // one block from the buffer at b0: the channel fragments and the first
+    // token fragment, its products, then the requests of a later block
+    // (`after`, so that they leave while the matrix core works), then the
+    // other token fragments and their products
+    auto compute = [&](uint32_t b0, auto after) {
+        const uint32_t al = b0 + a_row * kGroup + c_lo, ah = b0 + a_row * kGroup + c_hi;
+        const uint32_t bl = b0 + T::A_BYTES + b_row * kGroup + c_lo, bh = b0 + T::A_BYTES + b_row * kGroup + c_hi;
+        v4i a[2], b[T::FN][2];
         v8i bf[T::FN];
+        if constexpr (FMT == FMT_BLOCK) {
+            v4i sa[T::FM];
+            float swt;
+            const uint32_t sbase = b0 + T::A_BYTES + T::B_BYTES;
+            lds_frags_first_scaled<T::FM>(a, b, sa, swt, al, ah, bl, bh, sbase + (wm * T::WM + 4 * quarter) * 4,
+                                          sbase + 4 * 64 * 4);
 #pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn) {
-            const uint8_t *p = base + b_frag + fn * 16 * 16;
-            bf[fn] = join(*reinterpret_cast<const uint4 *>(p),
-                          *reinterpret_cast<const uint4 *>(p + 4 * T::PB * 16));
-        }
-        const float sw = sw_now;
+            for (int fn = 0; fn < T::FN; ++fn) bf[fn] = join4(b[fn][0], b[fn][1]);
 #pragma unroll
-        for (int fm = 0; fm < T::FM; ++fm) {
-            const uint8_t *p = base + a_frag + fm * 16 * 16;
-            const v8i af = join(*reinterpret_cast<const uint4 *>(p),
-                                *reinterpret_cast<const uint4 *>(p + 4 * T::PA * 16));
-            if constexpr (FMT == FMT_BLOCK) {
+            for (int fm = 0; fm < T::FM; ++fm) {
+                if (fm > 0) lds_frag(a, al + fm * 16 * kGroup, ah + fm * 16 * kGroup);
                 // this block's token scales for the lane's 4 rows, times the
                 // weight block's scale
-                const float4 sa = *reinterpret_cast<const float4 *>(
-                    base + T::A_BYTES + T::B_BYTES + (wm * T::WM + fm * 16 + 4 * quarter) * 4);
-                const float c0 = sa.x * sw, c1 = sa.y * sw, c2 = sa.z * sw, c3 = sa.w * sw;
+                const v8i af = join4(a[0], a[1]);
+                const float c0 = __int_as_float(sa[fm][0]) * swt, c1 = __int_as_float(sa[fm][1]) * swt;
+                const float c2 = __int_as_float(sa[fm][2]) * swt, c3 = __int_as_float(sa[fm][3]) * swt;
 #pragma unroll
                 for (int fn = 0; fn < T::FN; ++fn) {
                     const v4f p4 = block_mma<FMT>(af, bf[fn], v4f{0, 0, 0, 0});
@@ -193,35 +253,66 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmLaunch g) {
                     acc[fm][fn][2] += p4[2] * c2;
                     acc[fm][fn][3] += p4[3] * c3;
                 }
-            } else {
+                if (fm == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    after();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+            lds_frags_first(a, b, al, ah, bl, bh);
+#pragma unroll
+            for (int fn = 0; fn < T::FN; ++fn) bf[fn] = join4(b[fn][0], b[fn][1]);
+#pragma unroll
+            for (int fm = 0; fm < T::FM; ++fm) {
+                if (fm > 0) lds_frag(a, al + fm * 16 * kGroup, ah + fm * 16 * kGroup);
+                const v8i af = join4(a[0], a[1]);
 #pragma unroll
                 for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = block_mma<FMT>(af, bf[fn], acc[fm][fn]);
+                if (fm == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    after();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };
 
-    // ---- main loop: STAGES blocks in flight, two LDS buffers, one barrier
-    // per block.  Buffer j & 1 is rewritten at block j only after every wave
-    // has passed the barrier of block j - 1, i.e. finished computing block
-    // j - 2 from it.  Staging, the barrier and the requests run on every
-    // pass (past the range they move zeros), so the waits count exactly;
-    // only the computation is skipped there.
-    // (the scheduling barriers keep the stages' requests in issue order)
+    // ---- main loop.  At block j the requests of blocks j .. j + STAGES - 2
+    // are in flight; wait until only the younger STAGES - 2 blocks' are, then
+    // the barrier makes block j visible to every wave and tells that every
+    // wave has finished block j - 1, whose buffer then takes block
+    // j + STAGES - 1.  The barrier is a bare one (every wave has waited for
+    // its own copies, and its reads of a buffer completed inside its
+    // fragment-read blocks): a fence would wait for the copies in flight as
+    // well.  Every pass issues its requests, past the range too (they are
+    // out of range), so the waits count exactly; only the products are
+    // skipped there.  Unrolled by STAGES, so the buffers' addresses are
+    // constants.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)lds;   // LDS address of the ring
 #pragma unroll
-    for (int st = 0; st < T::STAGES; ++st) {
-        request(st, st);
+    for (int st = 0; st < T::STAGES - 1; ++st) {
+        issue(st, lds0 + st * T::BUF_BYTES);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int j0 = 0; j0 < nsteps; j0 += T::STAGES) {
 #pragma unroll
-        for (int st = 0; st < T::STAGES; ++st) {
-            const int j = j0 + st;
-            stage(st, j & 1);
-            __syncthreads();
-            request(st, j + T::STAGES);
-            if (j < nsteps) compute(j & 1);
+        for (int u = 0; u < T::STAGES; ++u) {
+            const int j = j0 + u;
+            const uint32_t next = lds0 + ((u + T::STAGES - 1) % T::STAGES) * T::BUF_BYTES;
+            __builtin_amdgcn_s_waitcnt(vmcnt_only((T::STAGES - 2) * T::REQ));
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            auto req = [&]() { issue(j + T::STAGES - 1, next); };
+            if (j < nsteps) compute(lds0 + u * T::BUF_BYTES, req);
+            else req();
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // the past-the-end copies still in flight land in LDS before the
+    // workgroup can end
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 
     // ---- epilogue.  Lane layout of a 16x16 result: channel r16, tokens
     // 4 * quarter + i.
