@@ -171,6 +171,79 @@ __device__ __forceinline__ void wait_memory_idle() {
 // 8-byte chunk cl (0, 1, ... along the K range) of row `row`
 __device__ __forceinline__ int stage_offset8(int cl, int row, int RS) { return row * RS * 16 + cl * 8; }
 
+// The last partition of a split-K tile adds the nsplit slices of its
+// rows x cols outputs at (m0, n0) (slice z at part + z * slice, row stride
+// N; cols a multiple of 4) in partition order, hands every group of 4
+// consecutive outputs to emit(m, n, v[4]), and leaves the slices zero.  The
+// slices were written by other workgroups, possibly on other XCDs, with
+// device-coherent stores, so they are read with device-coherent loads
+// (8 bytes each); a batch of 4 groups x 4 partitions is requested before
+// any of it is used, so the reduction takes one memory round trip per
+// batch rather than one per output.
+template <typename acc_s, typename Emit>
+__device__ __forceinline__ void reduce_slices(acc_s *part, int64_t slice, int N, int m0, int n0, int rows,
+                                              int cols, int nsplit, int tid, int nthreads, Emit emit) {
+    constexpr int GB = 4;   // groups of 4 outputs per thread and batch
+    constexpr int ZB = 4;   // partitions per batch
+    typedef unsigned long long u64;
+    const int cols4 = cols >> 2;
+    const int groups = rows * cols4;
+    for (int g0 = tid; g0 < groups; g0 += nthreads * GB) {
+        int64_t idx[GB];
+        bool ok[GB];
+#pragma unroll
+        for (int b = 0; b < GB; ++b) {
+            const int gi = g0 + b * nthreads;
+            ok[b] = gi < groups;
+            const int r = ok[b] ? gi / cols4 : 0, c = ok[b] ? gi - r * cols4 : 0;
+            idx[b] = (int64_t)(m0 + r) * N + n0 + 4 * c;
+        }
+        acc_s v[GB][4];
+#pragma unroll
+        for (int b = 0; b < GB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[b][i] = 0;
+        for (int z0 = 0; z0 < nsplit; z0 += ZB) {
+            u64 w[ZB][GB][2];
+#pragma unroll
+            for (int zz = 0; zz < ZB; ++zz)
+#pragma unroll
+                for (int b = 0; b < GB; ++b) {
+                    const bool live = ok[b] && z0 + zz < nsplit;
+                    const u64 *p = reinterpret_cast<const u64 *>(part + (int64_t)(z0 + zz) * slice + idx[b]);
+                    w[zz][b][0] = live ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+                    w[zz][b][1] = live ? __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+                }
+#pragma unroll
+            for (int zz = 0; zz < ZB; ++zz) {
+                if (z0 + zz >= nsplit) break;
+#pragma unroll
+                for (int b = 0; b < GB; ++b)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t lo = (uint32_t)w[zz][b][h], hi = (uint32_t)(w[zz][b][h] >> 32);
+                        acc_s a0, a1;
+                        __builtin_memcpy(&a0, &lo, 4);
+                        __builtin_memcpy(&a1, &hi, 4);
+                        v[b][2 * h] += a0;
+                        v[b][2 * h + 1] += a1;
+                    }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < GB; ++b) {
+            if (!ok[b]) continue;
+            const int gi = g0 + b * nthreads, r = gi / cols4, c = gi - r * cols4;
+            emit(m0 + r, n0 + 4 * c, v[b]);
+            for (int z = 0; z < nsplit; ++z) {   // leave the workspace zero
+                u64 *p = reinterpret_cast<u64 *>(part + (int64_t)z * slice + idx[b]);
+                __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
 // s_waitcnt operand that waits until at most n vector memory requests are
 // outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -685,22 +758,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     }
     __syncthreads();
     if (!s_last) return;
-    const int tn = min(TN, N - n_tile0);
-    for (int e = threadIdx.x; e < R * tn; e += nthreads) {
-        const int m = m0 + e / tn;
-        const int n = n_tile0 + e % tn;
-        const int64_t idx = (int64_t)m * N + n;
-        acc_s v = 0;
-        for (int z = 0; z < g.nsplit; ++z)
-            v += __hip_atomic_load(&part[z * slice + idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int z = 0; z < g.nsplit; ++z)   // leave the workspace zero
-            __hip_atomic_store(&part[z * slice + idx], (acc_s)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        float o;
-        if constexpr (FMT == FMT_BLOCK) o = v;
-        else if constexpr (FUSE) o = ((float)v * s_rowscale[m - m0]) * g.wsc[n];
-        else o = ((float)v * g.xs[m]) * g.wsc[n];
-        store1(idx, o, (int)v);
-    }
+    const int tn = min(TN, N - n_tile0);   // a multiple of 16
+    reduce_slices(part, slice, N, m0, n_tile0, R, tn, g.nsplit, (int)threadIdx.x, nthreads,
+                  [&](int m, int n, const acc_s (&v)[4]) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) {
+                          float o;
+                          if constexpr (FMT == FMT_BLOCK) o = v[i];
+                          else if constexpr (FUSE) o = ((float)v[i] * s_rowscale[m - m0]) * g.wsc[n + i];
+                          else o = ((float)v[i] * g.xs[m]) * g.wsc[n + i];
+                          store1((int64_t)m * N + n + i, o, (int)v[i]);
+                      }
+                  });
     if (threadIdx.x == 0)
         __hip_atomic_store(&g.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

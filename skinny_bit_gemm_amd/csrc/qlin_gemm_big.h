@@ -374,17 +374,11 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     }
     __syncthreads();
     if (!s_last) return;
-    for (int e = t; e < rows_a * rows_b; e += kBigThreads) {
-        const int m = m0 + e / rows_b;
-        const int n = n0 + e % rows_b;
-        const int64_t idx = (int64_t)m * N + n;
-        acc_s v = 0;
-        for (int zz = 0; zz < g.nsplit; ++zz)
-            v += __hip_atomic_load(&part[zz * slice + idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int zz = 0; zz < g.nsplit; ++zz)
-            __hip_atomic_store(&part[zz * slice + idx], (acc_s)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        store1(idx, out_value(v, m, n), (int)v);
-    }
+    reduce_slices(part, slice, N, m0, n0, rows_a, rows_b, g.nsplit, t, kBigThreads,
+                  [&](int m, int n, const acc_s (&v)[4]) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) store1((int64_t)m * N + n + i, out_value(v[i], m, n + i), (int)v[i]);
+                  });
     if (t == 0) __hip_atomic_store(&g.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
