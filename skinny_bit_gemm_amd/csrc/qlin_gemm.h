@@ -693,32 +693,60 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             if (kw != 0) return;
             unsigned long long *ws64 = static_cast<unsigned long long *>(g.acc_ws);
             const unsigned long long kUnit = 1ull << 52, kHalf = 1ull << 51;
+            // per 16-token fragment: all of the lane's atomics first (one
+            // round trip: the addends and addresses are all formed before the
+            // first atomic, so that none waits for another; elements past M
+            // or N are masked off), then the outputs of the elements this
+            // partition completes
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                if (nsub[r] >= N) continue;
+            for (int mt = 0; mt < MT; ++mt) {
+                unsigned long long old[NR][4], add[NR][4];
+                long long val[NR][4];
+                unsigned long long *dst[NR][4];
+                bool live[NR][4];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = token_of(mt, i);
+                        const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
+                        if constexpr (FMT == FMT_I8) val[r][i] = (long long)acc[r][mt][i];
+                        else val[r][i] = (long long)(acc[r][mt][i] * 262144.0f);
+                        live[r][i] = m < M && nsub[r] < N;
+                        add[r][i] = (unsigned long long)(val[r][i] + (long long)kUnit);
+                        // (kept in a register of its own: formed inside the
+                        // masked branch, every addend would reuse one
+                        // register and each atomic would wait for the last)
+                        asm volatile("" : "+v"(add[r][i]));
+                        dst[r][i] = &ws64[(int64_t)m * N + n];
+                        old[r][i] = 0;
+                    }
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (live[r][i])
+                            old[r][i] = __hip_atomic_fetch_add(dst[r][i], add[r][i], __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    if (nsub[r] >= N) continue;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int m = token_of(mt, i);
                         const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
                         if (m >= M) continue;
                         const int64_t idx = (int64_t)m * N + n;
-                        long long v;
-                        if constexpr (FMT == FMT_I8) v = (long long)acc[r][mt][i];
-                        else v = (long long)(acc[r][mt][i] * 262144.0f);
-                        const unsigned long long old = __hip_atomic_fetch_add(
-                            &ws64[idx], (unsigned long long)(v + (long long)kUnit), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
-                        const unsigned long long before = (old + kHalf) >> 52;
+                        const unsigned long long before = (old[r][i] + kHalf) >> 52;
                         if (before != (unsigned long long)(g.nsplit - 1)) continue;
-                        const long long total = (long long)(old - before * kUnit) + v;
+                        const long long total = (long long)(old[r][i] - before * kUnit) + val[r][i];
                         float t;
                         if constexpr (FMT == FMT_I8) t = (float)total;
                         else t = (float)((double)total * (1.0 / 262144.0));
                         store1(idx, scaled(t, r, mt, i), (int)total);
                         __hip_atomic_store(&ws64[idx], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
+                }
             }
             return;
         }
