@@ -174,6 +174,48 @@ qlin_status qlin_workspace_bytes(qlin_format fmt, int M, int N, int K, const qli
 /* Checks a schedule against (fmt, M, N, K) without launching anything. */
 qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qlin_config *cfg);
 
+/* Grouped (mixture-of-experts) GEMM: `groups` independent products of the
+ * same shape in one launch, group e computing y_e = dequant(xq_e . wq_e^T).
+ * The pages name MoE layers as the next target ("Helion gives vLLM's linear
+ * backend a reported 10%+ throughput lift on some workloads", section
+ * "Future work", model coverage); each group's product is the one of
+ * section "Kernel Implementation" ("Building a High-Performance and
+ * Portable vLLM Linear Backend with Helion").
+ *   group_offsets  device int32 [groups + 1], non-decreasing, from 0 to
+ *                  total_rows: group e owns rows [off[e], off[e+1]) of xq,
+ *                  x_scales and y.  Read by the kernel, so a captured graph
+ *                  can be replayed after the routing changes.  A group
+ *                  with no rows reads none of its weights.
+ *   total_rows     rows of xq / x_scales / y (0: nothing is enqueued)
+ *   max_group_rows bound on any group's rows; sizes the grid (rows of a
+ *                  group past it are not computed).  In decode with top-k
+ *                  routing, the token count is such a bound.
+ *   xq, x_scales   [total_rows, K] codes and their scales (qlin_quantize_act
+ *                  layouts), rows grouped by group
+ *   wq, w_scales   [groups][N][K] codes and [groups][N] (or
+ *                  [groups][N/128][K/128] for QLIN_BLOCK_FP8) scales
+ *   y              [total_rows, N]
+ *   cfg            NULL: qlin_grouped_select_variant's rule; otherwise
+ *                  forced (tile_m 16 or 32, fuse_quant 0)
+ *   workspace      as qlin_gemm, qlin_grouped_workspace_bytes(...) bytes
+ * Errors as qlin_gemm, plus QLIN_ERR_SHAPE for groups < 1, total_rows < 0,
+ * max_group_rows < 1 or more than 65535 group x token tiles. */
+qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const int *group_offsets,
+                              int total_rows, int max_group_rows, const void *xq,
+                              const float *x_scales, const void *wq, const float *w_scales, void *y,
+                              qlin_out_type out_type, const qlin_config *cfg, void *workspace,
+                              size_t ws_bytes, void *stream);
+
+/* The grouped launches' built-in schedule (no table: the groups already
+ * fill the GPU): Swap-AB, 16- or 32-token tiles, 64 channels by 4 waves, no
+ * split. */
+qlin_status qlin_grouped_select_variant(qlin_format fmt, int groups, int N, int K, int max_group_rows,
+                                        qlin_config *out);
+
+/* Workspace bytes qlin_grouped_gemm needs (0 without split-K). */
+qlin_status qlin_grouped_workspace_bytes(qlin_format fmt, int groups, int N, int K, int total_rows,
+                                         int max_group_rows, const qlin_config *cfg, size_t *bytes);
+
 /* Selection table.  qlin_load_table parses a text table (replacing any loaded
  * one; path NULL = the table installed next to the library); the table is
  * immutable afterwards, so lookups are thread-safe.  qlin_set_strict(1)

@@ -207,6 +207,32 @@ def linear(fmt: int, x_bf16, qw, sw, want_acc: bool = False):
     return qa, sa, ref
 
 
+def grouped_gemm(fmt: int, offsets, qa, sa, qw, sw, want_acc: bool = False):
+    """Grouped product: rows offsets[e] .. offsets[e+1] - 1 of (qa, sa) times
+    the e-th weights (qw[e], sw[e]), each group exactly as gemm(); the rows
+    come back in the same order.  A mixture-of-experts layer is this product
+    over the experts' row groups ("Helion gives vLLM's linear backend a
+    reported 10%+ throughput lift on some workloads", section "Future
+    work"; the product itself is "Building a High-Performance and Portable
+    vLLM Linear Backend with Helion", section "Kernel Implementation")."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    M, N = int(offsets[-1]), np.asarray(qw).shape[1]
+    ref = np.zeros((M, N), dtype=np.float64)
+    acc = np.zeros((M, N), dtype=np.int32) if (want_acc and fmt == W8A8_INT8) else None
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        out = gemm(fmt, qa[lo:hi], sa[lo:hi], qw[e], sw[e], want_acc=want_acc)
+        if want_acc:
+            ref[lo:hi] = out[0]
+            if acc is not None:
+                acc[lo:hi] = out[1]
+        else:
+            ref[lo:hi] = out
+    return (ref, acc) if want_acc else ref
+
+
 def round_bf16(v) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float64)
     out = np.empty(v.shape, dtype=np.uint16)

@@ -31,6 +31,7 @@ EXPORTS = (
     "qlin_workspace_bytes", "qlin_validate_config", "qlin_load_table", "qlin_set_strict",
     "qlin_table_entries", "qlin_graph_begin", "qlin_graph_end", "qlin_graph_launch",
     "qlin_graph_destroy", "qlin_status_str", "qlin_abi_version", "qlin_last_hip_error",
+    "qlin_grouped_gemm", "qlin_grouped_select_variant", "qlin_grouped_workspace_bytes",
 )
 
 
@@ -92,6 +93,11 @@ def lib():
         L.qlin_workspace_bytes.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config),
                                            ctypes.POINTER(_SZ)]
         L.qlin_validate_config.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config)]
+        L.qlin_grouped_gemm.argtypes = [_I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _I,
+                                        ctypes.POINTER(qlin_config), _P, _SZ, _P]
+        L.qlin_grouped_select_variant.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(qlin_config)]
+        L.qlin_grouped_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(qlin_config),
+                                                   ctypes.POINTER(_SZ)]
         L.qlin_load_table.argtypes = [ctypes.c_char_p]
         L.qlin_set_strict.argtypes = [_I]
         L.qlin_table_entries.argtypes = []
@@ -178,6 +184,34 @@ def qlin_workspace_bytes(fmt, M, N, K, cfg=None) -> int:
     st = lib().qlin_workspace_bytes(fmt, M, N, K, ctypes.byref(cfg) if cfg is not None else None,
                                     ctypes.byref(out))
     _check(st, "qlin_workspace_bytes", True)
+    return int(out.value)
+
+
+def qlin_grouped_gemm(fmt, groups, N, K, group_offsets, total_rows, max_group_rows, xq, x_scales, wq,
+                      w_scales, y, out_type=QLIN_OUT_BF16, cfg=None, workspace=None, ws_bytes=None,
+                      stream=None, raise_on_error=True):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None and \
+            not isinstance(workspace, int) else 0
+    cptr = ctypes.byref(cfg) if cfg is not None else None
+    st = lib().qlin_grouped_gemm(fmt, groups, N, K, _ptr(group_offsets), total_rows, max_group_rows,
+                                 _ptr(xq), _ptr(x_scales), _ptr(wq), _ptr(w_scales), _ptr(y), out_type,
+                                 cptr, _ptr(workspace), ws_bytes, _stream(stream))
+    return _check(st, "qlin_grouped_gemm", raise_on_error)
+
+
+def qlin_grouped_select_variant(fmt, groups, N, K, max_group_rows) -> qlin_config:
+    out = qlin_config()
+    st = lib().qlin_grouped_select_variant(fmt, groups, N, K, max_group_rows, ctypes.byref(out))
+    _check(st, "qlin_grouped_select_variant", True)
+    return out
+
+
+def qlin_grouped_workspace_bytes(fmt, groups, N, K, total_rows, max_group_rows, cfg=None) -> int:
+    out = _SZ(0)
+    st = lib().qlin_grouped_workspace_bytes(fmt, groups, N, K, total_rows, max_group_rows,
+                                            ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out))
+    _check(st, "qlin_grouped_workspace_bytes", True)
     return int(out.value)
 
 

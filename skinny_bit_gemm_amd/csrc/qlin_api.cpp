@@ -272,6 +272,7 @@ static GemmLaunch launch_args(const Plan &p, int M, int N, int K, const void *wq
     g.m_tiles = p.m_tiles;
     g.nw = p.nw;
     g.kw = p.kw;
+    g.slice = (int64_t)M * N;
     return g;
 }
 
@@ -327,6 +328,89 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
         g.xs = x_scales;
     }
     return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, p.xc, g, p.lds_bytes, s));
+}
+
+// ---------------------------------------------------------------- grouped
+
+// Built-in rule for grouped launches.  The groups already give the grid
+// many workgroups (active groups x channel tiles), so no split: 16- or
+// 32-token tiles (the largest group decides), Swap-AB, 64-column tiles of
+// four waves with two K waves.
+static void grouped_default_config(int max_group_rows, qlin_config *c) {
+    *c = qlin_config{1, 1, max_group_rows <= 16 ? 16 : 32, 64, 4, 2, 0, 0};
+}
+
+// Plans a grouped launch; the workspace holds one arrival counter per
+// (group, token tile, channel tile) and the split-K sums of all rows.
+static qlin_status grouped_plan(qlin_format fmt, int groups, int N, int K, int total_rows,
+                                int max_group_rows, const qlin_config *cfg, qlin_config *c, Plan *p) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    if (groups < 1 || groups > kMaxDim || total_rows < 0 || total_rows > kMaxDim || max_group_rows < 1)
+        return QLIN_ERR_SHAPE;
+    qlin_status st = shape_ok(fmt, max_group_rows, N, K);
+    if (st != QLIN_OK) return st;
+    if (cfg) *c = *cfg;
+    else grouped_default_config(max_group_rows, c);
+    // the skinny kernel only (16- or 32-token tiles), codes quantized beforehand
+    if (c->tile_m > 32 || c->fuse_quant != 0) return QLIN_ERR_INVALID_ARG;
+    st = make_plan(fmt, max_group_rows, N, K, *c, false, p);
+    if (st != QLIN_OK) return st;
+    if ((int64_t)groups * p->m_tiles > 65535) return QLIN_ERR_SHAPE;   // grid y
+    if (p->nsplit > 1) {
+        p->ws_counter_bytes = align256((size_t)groups * p->m_tiles * p->n_tiles * 4);
+        const size_t sums = p->packed ? (size_t)total_rows * N * 8 : (size_t)p->nsplit * total_rows * N * 4;
+        p->ws_bytes = p->ws_counter_bytes + align256(sums);
+    } else {
+        p->ws_counter_bytes = 0;
+        p->ws_bytes = 0;
+    }
+    return QLIN_OK;
+}
+
+qlin_status qlin_grouped_select_variant(qlin_format fmt, int groups, int N, int K, int max_group_rows,
+                                        qlin_config *out) {
+    if (!out) return QLIN_ERR_INVALID_ARG;
+    Plan p;
+    return grouped_plan(fmt, groups, N, K, 0, max_group_rows, nullptr, out, &p);
+}
+
+qlin_status qlin_grouped_workspace_bytes(qlin_format fmt, int groups, int N, int K, int total_rows,
+                                         int max_group_rows, const qlin_config *cfg, size_t *bytes) {
+    if (!bytes) return QLIN_ERR_INVALID_ARG;
+    qlin_config c;
+    Plan p;
+    const qlin_status st = grouped_plan(fmt, groups, N, K, total_rows, max_group_rows, cfg, &c, &p);
+    if (st != QLIN_OK) return st;
+    *bytes = p.ws_bytes;
+    return QLIN_OK;
+}
+
+qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const int *group_offsets,
+                              int total_rows, int max_group_rows, const void *xq, const float *x_scales,
+                              const void *wq, const float *w_scales, void *y, qlin_out_type out_type,
+                              const qlin_config *cfg, void *workspace, size_t ws_bytes, void *stream) {
+    if (out_type != QLIN_OUT_BF16 && out_type != QLIN_OUT_F32_ACC && out_type != QLIN_OUT_I32_ACC)
+        return QLIN_ERR_INVALID_ARG;
+    if (out_type == QLIN_OUT_I32_ACC && fmt != QLIN_W8A8_INT8) return QLIN_ERR_INVALID_ARG;
+    qlin_config c;
+    Plan p;
+    qlin_status st = grouped_plan(fmt, groups, N, K, total_rows, max_group_rows, cfg, &c, &p);
+    if (st != QLIN_OK) return st;
+    if (!group_offsets || !xq || !x_scales || !wq || !w_scales || !y) return QLIN_ERR_INVALID_ARG;
+    if (!aligned4(group_offsets) || !aligned16(xq) || !aligned16(wq) || !aligned16(y) ||
+        !aligned4(x_scales) || !aligned4(w_scales))
+        return QLIN_ERR_ALIGNMENT;
+    if (p.ws_bytes && (!workspace || ws_bytes < p.ws_bytes)) return QLIN_ERR_WORKSPACE;
+    if (p.ws_bytes && !aligned16(workspace)) return QLIN_ERR_ALIGNMENT;
+    if (total_rows == 0) return QLIN_OK;
+    GemmLaunch g = launch_args(p, total_rows, N, K, wq, w_scales, y, out_type, workspace);
+    g.xq = static_cast<const uint8_t *>(xq);
+    g.xs = x_scales;
+    g.group_off = group_offsets;
+    g.group_mt = p.m_tiles;
+    g.m_tiles = groups * p.m_tiles;   // grid y
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, 0, g, p.lds_bytes,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 struct qlin_graph_s {

@@ -269,7 +269,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     const int nw = wave % g.nw, kw = wave / g.nw;
     const int TN = 16 * NR * g.nw;
     const int n_tile0 = blockIdx.x * TN;
-    const int m0 = blockIdx.y * 16 * MT;
+    // grouped launch: blockIdx.y = group * group_mt + token tile; the
+    // group's rows, weights, scales, output rows and split-K sums take the
+    // place of the call's (a group with no rows in this tile reads nothing)
+    int mtile = blockIdx.y;
+    if (g.group_off) {
+        const int e = blockIdx.y / g.group_mt;
+        mtile = blockIdx.y - e * g.group_mt;
+        const int lo = min(max(g.group_off[e], 0), g.M);
+        const int hi = min(max(g.group_off[e + 1], lo), g.M);
+        if (mtile * 16 * MT >= hi - lo) return;
+        const int Gk = (g.K + kGroup - 1) / kGroup;
+        g.xq += (int64_t)lo * g.K;
+        g.xs += (int64_t)lo * (FMT == FMT_BLOCK ? Gk : 1);
+        g.y = static_cast<uint8_t *>(g.y) + (int64_t)lo * g.N * (g.out_type == QLIN_OUT_BF16 ? 2 : 4);
+        g.wq += (int64_t)e * g.N * g.K;
+        g.wsc += (int64_t)e * (FMT == FMT_BLOCK ? (int64_t)(g.N / kGroup) * Gk : g.N);
+        if (g.acc_ws) g.acc_ws = static_cast<uint8_t *>(g.acc_ws) + (int64_t)lo * g.N * (g.packed ? 8 : 4);
+        g.M = hi - lo;
+    }
+    const int m0 = mtile * 16 * MT;
     const int kb_begin = blockIdx.z * g.kb_per_split;
     const int kb_end = min(g.nkb, kb_begin + g.kb_per_split);
     const int M = g.M, N = g.N, K = g.K;
@@ -759,7 +778,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     // is deterministic), writes the output, and zeroes the slices and the
     // counter.
     acc_s *part = static_cast<acc_s *>(g.acc_ws);
-    const int64_t slice = (int64_t)M * N;
+    const int64_t slice = g.slice;
     if (kw == 0) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {

@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     // arrival; the last one adds the slices in partition order, writes the
     // output and leaves slices and counter zero.
     acc_s *part = static_cast<acc_s *>(g.acc_ws);
-    const int64_t slice = (int64_t)M * N;
+    const int64_t slice = g.slice;
 #pragma unroll
     for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll

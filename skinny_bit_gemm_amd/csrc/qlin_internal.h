@@ -39,6 +39,12 @@ struct GemmLaunch {
     int packed;          // split-K through packed 64-bit integer atomics (exact formats)
     int n_tiles, m_tiles;
     int nw, kw;          // waves along N and along K
+    int64_t slice;       // split-K slice stride in elements (M x N; total rows x N when grouped)
+    // grouped launches (mixture of experts): group e's rows are
+    // [group_off[e], group_off[e + 1]) of the call's M rows, its weights and
+    // scales the e-th of the call's; grid y = groups x group_mt token tiles
+    const int *group_off;
+    int group_mt;
 };
 
 // Derived launch geometry for (fmt, M, N, K, cfg).

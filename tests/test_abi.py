@@ -286,3 +286,29 @@ def test_one_hip_runtime_is_mapped():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
                          check=True).stdout.strip().splitlines()[-1]
     assert out == "1"
+
+
+def test_grouped_gemm_validation():
+    def gg(groups=4, N=256, K=512, off=A, total=9, maxr=4, cfg=None, ws=None, wsb=0, fmt=FP8, out=q.QLIN_OUT_BF16):
+        return q.qlin_grouped_gemm(fmt, groups, N, K, off, total, maxr, A, A, A, A, A, out, cfg, ws, wsb,
+                                   stream=0, raise_on_error=False)
+    assert gg(total=0) == OK                                   # nothing to do: no launch
+    assert gg(off=None, total=0) == EINVAL
+    assert gg(off=A + 2, total=0) == EALIGN
+    assert gg(groups=0, total=0) == ESHAPE
+    assert gg(total=-1) == ESHAPE
+    assert gg(maxr=0, total=0) == ESHAPE
+    assert gg(N=100, total=0) == ESHAPE
+    assert gg(fmt=BLK, N=192, total=0) == ESHAPE
+    assert gg(out=q.QLIN_OUT_I32_ACC, total=0) == EINVAL       # int32 sums: W8A8_INT8 only
+    assert gg(cfg=q.make_config(0, 1, 64, 128, 4, 1), total=0) == EINVAL   # large-M tiles: not grouped
+    assert gg(cfg=q.make_config(1, 1, 16, 32, 4, 4, 0, 1), total=0) == EINVAL   # codes come quantized
+    assert gg(groups=40000, maxr=32, cfg=q.make_config(1, 1, 16, 64, 4, 2), total=0) == ESHAPE   # grid y
+    split = q.make_config(1, 2, 16, 64, 4, 2)
+    need = q.qlin_grouped_workspace_bytes(FP8, 4, 256, 512, 9, 4, split)
+    assert need > 0 and q.qlin_grouped_workspace_bytes(FP8, 4, 256, 512, 9, 4) == 0
+    assert gg(cfg=split, ws=A, wsb=need - 1) == EWS
+    assert gg(cfg=split, ws=None, wsb=need) == EWS
+    c = q.qlin_grouped_select_variant(FP8, 128, 1536, 2048, 8)
+    assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.fuse_quant) == (1, 1, 16, 64, 0)
+    assert q.qlin_grouped_select_variant(I8, 128, 2048, 768, 32).tile_m == 32

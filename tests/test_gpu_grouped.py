@@ -1,0 +1,170 @@
+"""GPU parity of the grouped (mixture-of-experts) product against the oracle.
+
+Bars as for the dense product: codes and scales bit-exact, int8 int32
+accumulators bit-exact for every schedule, bf16 outputs within
+|y - ref| <= 1e-2 |ref| + 1e-3 max|ref|.  Routing is synthetic top-k
+(workloads.moe_routing), with empty groups; the offsets live on the device,
+so a captured graph is replayed after the routing changes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import skinny_bit_gemm_amd as q
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+from _gpu import DEV, as_u8, gpu_quant_act, to_dev, y_to_numpy  # noqa: E402
+
+FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
+FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.lib()
+    oracle.build()
+
+
+def cfg(swap=1, split=1, tile_m=16, tile_n=64, waves=4, k_waves=2, reduce=0):
+    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves, reduce, 0)
+
+
+SCHEDULES = {
+    "default": None,
+    "std": cfg(0, 1, 16, 32, 4, 4),
+    "swap_m32": cfg(1, 1, 32, 64, 4, 2),
+    "std_nw4": cfg(0, 1, 16, 128, 8, 2),
+    "split2": cfg(1, 2, 16, 64, 4, 2),
+    "split3_std": cfg(0, 3, 32, 32, 4, 4),
+}
+PACKED = {"packed2": cfg(1, 2, 16, 64, 4, 2, reduce=1), "packed4_std": cfg(0, 4, 16, 32, 4, 2, reduce=1)}
+
+
+def experts(fmt, E, N, K, seed):
+    """E quantized experts, [E][N][K] codes and their scales (oracle bytes,
+    which the device weight quantizer matches bit for bit)."""
+    qw, sw = zip(*[oracle.quant_weight(fmt, wl.random_weights(N, K, seed + e)) for e in range(E)])
+    return np.stack(qw), np.stack(sw)
+
+
+def run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, max_rows, c, out_type=q.QLIN_OUT_BF16):
+    total = int(offsets[-1])
+    dt = {q.QLIN_OUT_BF16: torch.int16, q.QLIN_OUT_I32_ACC: torch.int32}[out_type]
+    y = torch.full((total, N), -1, dtype=dt, device=DEV)    # sentinel: every row must be written
+    nb = q.qlin_grouped_workspace_bytes(fmt, E, N, K, total, max_rows, c)
+    work = torch.zeros(max(nb, 16), dtype=torch.uint8, device=DEV)
+    off = to_dev(offsets.astype(np.int32))
+    q.qlin_grouped_gemm(fmt, E, N, K, off, total, max_rows, xq, xs, wqd, wsd, y, out_type, c, work)
+    torch.cuda.synchronize()
+    assert not torch.any(work != 0), "workspace not left zero"
+    return y
+
+
+def check_case(fmt, E, N, K, T, topk, seed, c):
+    offsets, rows = wl.moe_routing(T, E, topk, seed)
+    x = wl.random_bf16((T, K), seed + 7)[rows]
+    xq, xs = gpu_quant_act(fmt, x)
+    qa, sa = oracle.quant_act(fmt, x)
+    assert np.array_equal(as_u8(xq), qa) and np.array_equal(xs.cpu().numpy().view(np.uint32), sa.view(np.uint32))
+    qw, sw = experts(fmt, E, N, K, 1000 * seed)
+    wqd, wsd = to_dev(qw), to_dev(sw)
+    print(f"[grouped] fmt={fmt} E={E} N={N} K={K} T={T} top{topk} cfg={c}", flush=True)
+    y = run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, T, c)
+    ref = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw)
+    ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
+    assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
+    if fmt == wl.W8A8_INT8:
+        _, acc = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw, want_acc=True)
+        yi = run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, T, c, q.QLIN_OUT_I32_ACC)
+        assert np.array_equal(yi.cpu().numpy(), acc), "int32 accumulators differ"
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("name", list(SCHEDULES))
+def test_grouped_schedules_match_oracle(fmt, name):
+    # 20 experts, top-3 of 13 tokens: 4 experts empty (the first and the last
+    # among them), a ragged channel tile (N = 384 over 64- and 128-column tiles)
+    check_case(fmt, 20, 384, 640, 13, 3, 1, SCHEDULES[name])
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
+@pytest.mark.parametrize("name", list(PACKED))
+def test_grouped_packed_reduction(fmt, name):
+    check_case(fmt, 9, 256, 1024, 6, 2, 2, PACKED[name])
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
+@pytest.mark.parametrize("tile_m", [16, 32])
+def test_grouped_ragged_k_and_many_rows(fmt, tile_m):
+    # K not a multiple of 128; 40 tokens top-2 of 4 experts: groups of 18 to
+    # 25 rows, so several token tiles per group with a ragged last one
+    check_case(fmt, 4, 256, 1040, 40, 2, 3, cfg(1, 1, tile_m, 64, 4, 2))
+
+
+def test_grouped_graph_replays_follow_new_routing():
+    """One captured graph; the offsets buffer (and the rows) change between
+    replays, the total row count stays T * topk, as in decode."""
+    fmt, E, N, K, T, topk = wl.W8A8_INT8, 16, 256, 512, 6, 2
+    qw, sw = experts(fmt, E, N, K, 77)
+    wqd, wsd = to_dev(qw), to_dev(sw)
+    total = T * topk
+    xq = torch.empty((total, K), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((total,), dtype=torch.float32, device=DEV)
+    off = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
+    y = torch.empty((total, N), dtype=torch.int32, device=DEV)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        q.qlin_graph_begin(st)
+        q.qlin_grouped_gemm(fmt, E, N, K, off, total, T, xq, xs, wqd, wsd, y, q.QLIN_OUT_I32_ACC, None, None,
+                            stream=st)
+        g = q.qlin_graph_end(st)
+    try:
+        for seed in range(4):
+            offsets, rows = wl.moe_routing(T, E, topk, seed)
+            x = wl.random_bf16((T, K), seed)[rows]
+            qa, sa = oracle.quant_act(fmt, x)
+            off.copy_(torch.from_numpy(offsets))
+            xq.copy_(torch.from_numpy(qa))
+            xs.copy_(torch.from_numpy(sa))
+            torch.cuda.synchronize()
+            q.qlin_graph_launch(g, st)
+            st.synchronize()
+            _, acc = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw, want_acc=True)
+            assert np.array_equal(y.cpu().numpy(), acc), f"replay {seed}"
+    finally:
+        q.qlin_graph_destroy(g)
+
+
+def test_grouped_moe_layer_shape():
+    """The 128-expert top-8 layer (gate_up: 1536 x 2048) at 4 tokens, with
+    the default schedule; only the active experts' weights are quantized."""
+    fmt, E, N, K, T, topk = wl.FP8_DYNAMIC, wl.MOE_EXPERTS, 1536, 2048, 4, wl.MOE_TOPK
+    offsets, rows = wl.moe_routing(T, E, topk, 5)
+    x = wl.activations(fmt, N, K, T)[rows]
+    xq, xs = gpu_quant_act(fmt, x)
+    qa, sa = oracle.quant_act(fmt, x)
+    qw = np.zeros((E, N, K), dtype=np.uint8)
+    sw = np.ones((E, N), dtype=np.float32)
+    active = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+    for e in active:
+        qw[e], sw[e] = oracle.quant_weight(fmt, wl.random_weights(N, K, 9000 + e))
+    y = run(fmt, offsets, xq, xs, to_dev(qw), to_dev(sw), E, N, K, T, None)
+    ref = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw)
+    ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
+    assert ok and len(active) > 16, (worst, len(active))
+
+
+def test_grouped_no_rows_is_a_no_op():
+    E, N, K = 4, 256, 512
+    y = torch.full((1, N), -1, dtype=torch.int16, device=DEV)
+    off = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
+    z = torch.zeros((E, N, K), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((E, N), dtype=torch.float32, device=DEV)
+    q.qlin_grouped_gemm(wl.FP8_DYNAMIC, E, N, K, off, 0, 4, z, s, z, s, y)
+    torch.cuda.synchronize()
+    assert torch.all(y == -1)

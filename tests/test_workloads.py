@@ -47,3 +47,25 @@ def test_tiny_case_and_byte_counts():
     assert wl.algorithmic_bytes(wl.W8A8_INT8, 1, 4096, 4096) == 16_805_892
     assert wl.algorithmic_bytes(wl.W8A8_INT8, 32, 4096, 4096) == 17_186_944
     assert wl.algorithmic_bytes(wl.BLOCK_FP8, 32, 51200, 5120) == 265_653_760
+
+
+def test_moe_routing_is_top_k_of_distinct_experts():
+    for T, E, k, seed in ((1, 128, 8, 0), (7, 16, 3, 1), (32, 128, 8, 2)):
+        offsets, rows = wl.moe_routing(T, E, k, seed)
+        assert offsets.dtype == np.int32 and rows.dtype == np.int32
+        assert offsets[0] == 0 and offsets[-1] == T * k and np.all(np.diff(offsets) >= 0)
+        assert np.array_equal(np.bincount(rows, minlength=T), np.full(T, k))   # k experts per token
+        for e in range(E):
+            grp = rows[offsets[e]:offsets[e + 1]]
+            assert len(set(grp.tolist())) == len(grp) and np.all(np.diff(grp) > 0)   # distinct, by token
+        o2, r2 = wl.moe_routing(T, E, k, seed)
+        assert np.array_equal(o2, offsets) and np.array_equal(r2, rows)
+
+
+def test_grouped_bytes_count_active_groups_only():
+    offsets = np.array([0, 2, 2, 5, 5], dtype=np.int32)        # groups 0 and 2 active, 5 rows
+    N, K = 256, 512
+    b = wl.grouped_algorithmic_bytes(wl.FP8_DYNAMIC, offsets, N, K)
+    assert b == 2 * (N * K + 4 * N) + 5 * K + 4 * 5 + 2 * 5 * N
+    bb = wl.grouped_algorithmic_bytes(wl.BLOCK_FP8, offsets, N, K)
+    assert bb == 2 * (N * K + 4 * 2 * 4) + 5 * K + 4 * 5 * 4 + 2 * 5 * N

@@ -130,6 +130,43 @@ def random_weights(N: int, K: int, seed: int, std: float = 0.02) -> np.ndarray:
     return rng.normal(0.0, std, size=(N, K)).astype(np.float32)
 
 
+# A mixture-of-experts layer of the 30B-class, 3B-active shape (hidden 2048,
+# 128 experts of width 768, top-8 routing): the grouped product's workload.
+# The pages name MoE layers as the next target ("Helion gives vLLM's linear
+# backend a reported 10%+ throughput lift on some workloads", section
+# "Future work"); they give no MoE shapes, so this is a representative one.
+MOE_EXPERTS = 128
+MOE_TOPK = 8
+MOE_LAYERS = (Layer("expert_gate_up", 1536, 2048), Layer("expert_down", 2048, 768))
+MOE_TOKENS = TUNED_M
+
+
+def moe_routing(T: int, E: int, topk: int, seed: int):
+    """Synthetic top-k routing of T tokens to E experts (each token picks topk
+    distinct experts uniformly at random; rng = default_rng([2, T, E, topk,
+    seed])).  Returns (offsets int32 [E + 1], rows int32 [T * topk]): group e
+    owns rows offsets[e] .. offsets[e+1] - 1, and grouped row i holds token
+    rows[i]'s activations.  Rows are ordered by expert, then token."""
+    rng = np.random.default_rng([2, T, E, topk, seed])
+    pairs = [(int(e), t) for t in range(T) for e in rng.choice(E, size=topk, replace=False)]
+    pairs.sort()
+    counts = np.bincount([e for e, _ in pairs], minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return offsets, np.array([t for _, t in pairs], dtype=np.int32)
+
+
+def grouped_algorithmic_bytes(fmt: int, offsets, N: int, K: int) -> int:
+    """Bytes a perfect grouped product moves: the weights and scales of the
+    groups that have rows, and every row's codes, scales and bf16 output."""
+    offsets = np.asarray(offsets)
+    active = int(np.count_nonzero(np.diff(offsets)))
+    rows = int(offsets[-1])
+    wsc = 4 * (N // 128) * (K // 128) if fmt == BLOCK_FP8 else 4 * N
+    asc = 4 * rows * (K // 128) if fmt == BLOCK_FP8 else 4 * rows
+    return active * (N * K + wsc) + rows * K + asc + 2 * rows * N
+
+
 def algorithmic_bytes(fmt: int, M: int, N: int, K: int) -> int:
     """Bytes a perfect GEMM moves: W, its scales, quantized A, its scales, bf16 Y."""
     if fmt == BLOCK_FP8:
