@@ -42,6 +42,12 @@ def parse():
     ap.add_argument("--sweep", default=None,
                     help="instead of the step: time the crossover sweep (8B-class shapes, forced "
                          "schedules and the table's pick) and write it (JSON) here")
+    ap.add_argument("--moe", default=None,
+                    help="write the grouped (mixture-of-experts) measurements to this JSON file and exit")
+    ap.add_argument("--moe-tokens", default=None, help="token counts of --moe (default: 1..32)")
+    ap.add_argument("--moe-layers", default=None, help="layers of --moe (default: all)")
+    ap.add_argument("--moe-schedules", default=None,
+                    help="schedules of --moe (rule, forced ones, per_expert_launches; default: all)")
     ap.add_argument("--sweep-formats", default="fp8_dynamic,w8a8_int8,block_fp8")
     ap.add_argument("--sweep-m", default="1,2,4,8,16,24,32,64,128,256,512")
     ap.add_argument("--no-read-ceiling", action="store_true",
@@ -135,6 +141,18 @@ def measured_traffic(workload):
     if rec.get("kernel_source_sha256") != ksha or rec.get("table_sha256") != tsha:
         return None
     return rec
+
+
+def calibrate_copy(nbytes):
+    """Three plain device copies of nbytes (reference dispatches for
+    scaling the HBM byte counters)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def capture(stream, fn):
@@ -277,6 +295,132 @@ def crossover_sweep(path, fmts, Ms):
                                              default=None) for f in sorted({k[0] for k in best})}}
 
 
+def moe_configs(q, fmt, T):
+    """Forced grouped schedules timed beside the built-in rule (None)."""
+    tm = 16 if T <= 16 else 32
+    red = 1 if fmt != 2 else 0   # packed atomics for the exact formats
+    return {"rule": None,
+            "swap_n32_kw4": q.make_config(1, 1, tm, 32, 4, 4),
+            "standard": q.make_config(0, 1, tm, 64, 4, 2),
+            "split2": q.make_config(1, 2, tm, 64, 4, 2, red),
+            "split4": q.make_config(1, 4, tm, 64, 4, 2, red)}
+
+
+def moe_bench(path, fmts, Ts, layers=None, schedules=None):
+    """Grouped GEMM over the 128-expert top-8 layers: one launch for all
+    experts, timed as a hipGraph of launches that each take another routing
+    and another copy of the expert weights (>= 2 GiB of copies in total, so
+    the 256 MiB Infinity Cache holds at most a small share of the experts a
+    launch reads).  Beside it, the same work as one dense launch per active
+    expert (the table's pick for that expert's row count)."""
+    import numpy as np
+    import torch
+    import skinny_bit_gemm_amd as q
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    q.lib()
+    st = torch.cuda.Stream()
+    E, topk = wl.MOE_EXPERTS, wl.MOE_TOPK
+    rows_out = []
+
+    def timed(fn, n):
+        fn()
+        g = capture(st, fn)
+        q.qlin_graph_launch(g, st)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(3):
+            q.qlin_graph_launch(g, st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        q.qlin_graph_destroy(g)
+        return e0.elapsed_time(e1) * 1e3 / (3 * n)
+
+    with torch.cuda.stream(st):
+        for fmt in fmts:
+            for L in wl.MOE_LAYERS:
+                if layers and L.name not in layers:
+                    continue
+                N, K = L.N, L.K
+                wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+                ws = torch.empty((E,) + tuple(q.scales_shape(fmt, N, K, True)), dtype=torch.float32, device=dev)
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(7000 + fmt)
+                for e in range(E):   # N(0, 0.02) master weights, drawn on the device
+                    w = torch.randn((N, K), generator=gen, device=dev) * 0.02
+                    q.qlin_quantize_weight(fmt, N, K, w, wq[e], ws[e], stream=st)
+                del w
+                C = max(2, -(-(2 << 30) // (E * N * K)))
+                copies = [wq] + [wq.clone() for _ in range(C - 1)]
+                for T in Ts:
+                    total = T * topk
+                    R = 2 * C   # launches per graph: routing i on copy i % C
+                    routes = [wl.moe_routing(T, E, topk, 100 + i) for i in range(R)]
+                    offs = [torch.from_numpy(o).to(dev) for o, _ in routes]
+                    x = torch.from_numpy(wl.random_bf16((total, K), 11).view(np.int16)).to(dev)
+                    xq = torch.empty((total, K), dtype=torch.uint8, device=dev)
+                    xs = torch.empty(q.scales_shape(fmt, total, K, False), dtype=torch.float32, device=dev)
+                    q.qlin_quantize_act(fmt, total, K, x, K, xq, xs, stream=st)
+                    y = torch.empty((total, N), dtype=torch.bfloat16, device=dev)
+                    nbytes = sum(wl.grouped_algorithmic_bytes(fmt, o, N, K) for o, _ in routes) / R
+                    active = sum(int(np.count_nonzero(np.diff(o))) for o, _ in routes) / R
+                    point = {"format": wl.FORMAT_NAMES[fmt], "layer": L.name, "N": N, "K": K, "T": T,
+                             "rows": total, "active_experts": active, "bytes_per_launch": round(nbytes)}
+                    for name, c in moe_configs(q, fmt, T).items():
+                        if schedules and name not in schedules:
+                            continue
+                        cfg = c if c is not None else q.qlin_grouped_select_variant(fmt, E, N, K, T)
+                        nb = q.qlin_grouped_workspace_bytes(fmt, E, N, K, total, T, cfg)
+                        work = torch.zeros(max(256, nb), dtype=torch.uint8, device=dev)
+                        us = timed(lambda: [q.qlin_grouped_gemm(fmt, E, N, K, offs[i], total, T, xq, xs,
+                                                                copies[i % C], ws, y, q.QLIN_OUT_BF16, cfg, work,
+                                                                stream=st) for i in range(R)], R)
+                        rows_out.append(dict(point, schedule=name, cfg=cfg.as_dict(), us=round(us, 3),
+                                             GBps=round(nbytes / us / 1e3, 1),
+                                             frac_hbm=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)))
+                        del work
+                    pts = lambda: [r for r in rows_out if r["format"] == point["format"] and r["layer"] == L.name
+                                   and r["T"] == T]
+                    if schedules and "per_expert_launches" not in schedules:
+                        print(f"[moe] {point['format']} {L.name} T={T} active={active:.1f}: " + ", ".join(
+                            f"{r['schedule']} {r['us']:.1f}us" for r in pts()), file=sys.stderr, flush=True)
+                        continue
+                    # one dense launch per active expert, on the same routings and copies
+                    launches = []
+                    for i, (o, _) in enumerate(routes):
+                        for e in range(E):
+                            lo, hi = int(o[e]), int(o[e + 1])
+                            if hi > lo:
+                                cfg = q.qlin_select_variant(fmt, hi - lo, N, K)
+                                nb = q.qlin_workspace_bytes(fmt, hi - lo, N, K, cfg)
+                                launches.append((i, lo, hi, e, cfg, nb))
+                    work = torch.zeros(max(256, max(l[5] for l in launches)), dtype=torch.uint8, device=dev)
+
+                    def per_expert():
+                        for i, lo, hi, e, cfg, _ in launches:
+                            q.qlin_gemm(fmt, hi - lo, N, K, xq[lo:hi], xs[lo:hi],
+                                        copies[i % C][e], ws[e], y[lo:hi], q.QLIN_OUT_BF16, cfg, work, stream=st)
+                    us = timed(per_expert, R)
+                    rows_out.append(dict(point, schedule="per_expert_launches", cfg=None, us=round(us, 3),
+                                         GBps=round(nbytes / us / 1e3, 1),
+                                         frac_hbm=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)))
+                    del work
+                    print(f"[moe] {point['format']} {L.name} T={T} active={active:.1f}: " + ", ".join(
+                        f"{r['schedule']} {r['us']:.1f}us" for r in pts()), file=sys.stderr, flush=True)
+                del copies, wq, ws
+                torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(rows_out, f, indent=1)
+    import math
+
+    def geomean(name):
+        v = [r["GBps"] for r in rows_out if r["schedule"] == name]
+        return round(math.exp(sum(map(math.log, v)) / len(v)), 1) if v else None
+    return {"mode": "moe", "points": len({(r["format"], r["layer"], r["T"]) for r in rows_out}), "file": path,
+            "geomean_rule_GBps": geomean("rule"), "geomean_per_expert_GBps": geomean("per_expert_launches")}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -290,6 +434,14 @@ def main():
 
     if args.workload not in wl.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; choose from {sorted(wl.WORKLOADS)}")
+    if args.moe:
+        fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
+        Ts = [int(t) for t in args.moe_tokens.split(",")] if args.moe_tokens else list(wl.MOE_TOKENS)
+        if args.calibrate_copy:
+            calibrate_copy(args.calibrate_copy)
+        print(json.dumps(moe_bench(args.moe, fmts, Ts, args.moe_layers and args.moe_layers.split(","),
+                                   args.moe_schedules and args.moe_schedules.split(","))), flush=True)
+        return
     if args.sweep:
         fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
         print(json.dumps(crossover_sweep(args.sweep, fmts, [int(m) for m in args.sweep_m.split(",")])),
@@ -300,12 +452,7 @@ def main():
     torch.cuda.set_device(dev)
     q.lib()
     if args.calibrate_copy:
-        src = torch.ones(args.calibrate_copy // 4, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate_copy(args.calibrate_copy)
 
     # quantized weights (GPU quantizer, offline and untimed), then rotating copies
     base = {}

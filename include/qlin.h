@@ -176,20 +176,20 @@ qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qli
 
 /* Grouped (mixture-of-experts) GEMM: `groups` independent products of the
  * same shape in one launch, group e computing y_e = dequant(xq_e . wq_e^T).
- * The pages name MoE layers as the next target ("Helion gives vLLM's linear
- * backend a reported 10%+ throughput lift on some workloads", section
- * "Future work", model coverage); each group's product is the one of
- * section "Kernel Implementation" ("Building a High-Performance and
- * Portable vLLM Linear Backend with Helion").
+ * The pages name MoE layers as the next target, and each group's product is
+ * the one they define ("Building a High-Performance and Portable vLLM
+ * Linear Backend with Helion", sections "Future work", model-coverage
+ * paragraph, and "Kernel Implementation").
  *   group_offsets  device int32 [groups + 1], non-decreasing, from 0 to
  *                  total_rows: group e owns rows [off[e], off[e+1]) of xq,
  *                  x_scales and y.  Read by the kernel, so a captured graph
  *                  can be replayed after the routing changes.  A group
  *                  with no rows reads none of its weights.
  *   total_rows     rows of xq / x_scales / y (0: nothing is enqueued)
- *   max_group_rows bound on any group's rows; sizes the grid (rows of a
- *                  group past it are not computed).  In decode with top-k
- *                  routing, the token count is such a bound.
+ *   max_group_rows the expected largest group: token tiles hold
+ *                  min(tile_m, max_group_rows) rows.  Larger groups are
+ *                  still computed whole, in more tiles.  In decode with
+ *                  top-k routing, the token count bounds every group.
  *   xq, x_scales   [total_rows, K] codes and their scales (qlin_quantize_act
  *                  layouts), rows grouped by group
  *   wq, w_scales   [groups][N][K] codes and [groups][N] (or
@@ -198,8 +198,11 @@ qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qli
  *   cfg            NULL: qlin_grouped_select_variant's rule; otherwise
  *                  forced (tile_m 16 or 32, fuse_quant 0)
  *   workspace      as qlin_gemm, qlin_grouped_workspace_bytes(...) bytes
+ * The grid covers ceil(total_rows / tile rows) + min(groups, total_rows)
+ * token tiles, a bound on the tiles of any routing; workgroups past the
+ * routing's own tiles exit without reading anything.
  * Errors as qlin_gemm, plus QLIN_ERR_SHAPE for groups < 1, total_rows < 0,
- * max_group_rows < 1 or more than 65535 group x token tiles. */
+ * max_group_rows < 1 or a grid of more than 65535 token tiles. */
 qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const int *group_offsets,
                               int total_rows, int max_group_rows, const void *xq,
                               const float *x_scales, const void *wq, const float *w_scales, void *y,
@@ -207,7 +210,8 @@ qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const i
                               size_t ws_bytes, void *stream);
 
 /* The grouped launches' built-in schedule (no table: the groups already
- * fill the GPU): Swap-AB, 16- or 32-token tiles, 64 channels by 4 waves, no
+ * fill the GPU): Swap-AB, 16- or 32-token tiles, 64 channels by 4 waves
+ * (32 channels by 4 K waves when max_group_rows <= 2 and K >= 2048), no
  * split. */
 qlin_status qlin_grouped_select_variant(qlin_format fmt, int groups, int N, int K, int max_group_rows,
                                         qlin_config *out);

@@ -211,10 +211,10 @@ def grouped_gemm(fmt: int, offsets, qa, sa, qw, sw, want_acc: bool = False):
     """Grouped product: rows offsets[e] .. offsets[e+1] - 1 of (qa, sa) times
     the e-th weights (qw[e], sw[e]), each group exactly as gemm(); the rows
     come back in the same order.  A mixture-of-experts layer is this product
-    over the experts' row groups ("Helion gives vLLM's linear backend a
-    reported 10%+ throughput lift on some workloads", section "Future
-    work"; the product itself is "Building a High-Performance and Portable
-    vLLM Linear Backend with Helion", section "Kernel Implementation")."""
+    over the experts' row groups; the pages name MoE models as future work
+    and give each group's product ("Building a High-Performance and Portable
+    vLLM Linear Backend with Helion", sections "Future work", model-coverage
+    paragraph, and "Kernel Implementation")."""
     offsets = np.asarray(offsets, dtype=np.int64)
     M, N = int(offsets[-1]), np.asarray(qw).shape[1]
     ref = np.zeros((M, N), dtype=np.float64)

@@ -1,6 +1,7 @@
 // qlin_api.cpp -- the C ABI: argument validation, schedule planning and
 // dispatch to the gfx950 kernels.  Every check runs before the first HIP
 // call, so a rejected call touches neither the device nor the stream.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <new>
@@ -335,13 +336,24 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
 // Built-in rule for grouped launches.  The groups already give the grid
 // many workgroups (active groups x channel tiles), so no split: 16- or
 // 32-token tiles (the largest group decides), Swap-AB, 64-column tiles of
-// four waves with two K waves.
-static void grouped_default_config(int max_group_rows, qlin_config *c) {
-    *c = qlin_config{1, 1, max_group_rows <= 16 ? 16 : 32, 64, 4, 2, 0, 0};
+// four waves with two K waves; with at most 2 rows per group and K >= 2048,
+// 32-column tiles with four K waves (twice the workgroups, each wave's K
+// range halved), which measured ~10% faster on 128-expert layers.
+static void grouped_default_config(int max_group_rows, int K, qlin_config *c) {
+    if (max_group_rows <= 2 && K >= 2048) *c = qlin_config{1, 1, 16, 32, 4, 4, 0, 0};
+    else *c = qlin_config{1, 1, max_group_rows <= 16 ? 16 : 32, 64, 4, 2, 0, 0};
+}
+
+// Token tiles of a grouped launch: tiles of min(tile_m, max_group_rows)
+// rows (the rows the LDS staging is sized for).  Group e has
+// ceil(rows_e / tile rows) of them, fewer than rows_e / tile rows + 1, so
+// ceil(total_rows / tile rows) + (groups with rows) bounds every routing.
+static int64_t grouped_grid_y(int groups, int total_rows, int group_rows) {
+    return (total_rows + (int64_t)group_rows - 1) / group_rows + std::min(groups, total_rows);
 }
 
 // Plans a grouped launch; the workspace holds one arrival counter per
-// (group, token tile, channel tile) and the split-K sums of all rows.
+// (token tile, channel tile) and the split-K sums of all rows.
 static qlin_status grouped_plan(qlin_format fmt, int groups, int N, int K, int total_rows,
                                 int max_group_rows, const qlin_config *cfg, qlin_config *c, Plan *p) {
     if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
@@ -350,14 +362,16 @@ static qlin_status grouped_plan(qlin_format fmt, int groups, int N, int K, int t
     qlin_status st = shape_ok(fmt, max_group_rows, N, K);
     if (st != QLIN_OK) return st;
     if (cfg) *c = *cfg;
-    else grouped_default_config(max_group_rows, c);
+    else grouped_default_config(max_group_rows, K, c);
     // the skinny kernel only (16- or 32-token tiles), codes quantized beforehand
     if (c->tile_m > 32 || c->fuse_quant != 0) return QLIN_ERR_INVALID_ARG;
     st = make_plan(fmt, max_group_rows, N, K, *c, false, p);
     if (st != QLIN_OK) return st;
-    if ((int64_t)groups * p->m_tiles > 65535) return QLIN_ERR_SHAPE;   // grid y
+    p->m_tiles = (int)std::min<int64_t>(grouped_grid_y(groups, total_rows, std::min(c->tile_m, max_group_rows)),
+                                        INT32_MAX);
+    if (p->m_tiles > 65535) return QLIN_ERR_SHAPE;   // grid y
     if (p->nsplit > 1) {
-        p->ws_counter_bytes = align256((size_t)groups * p->m_tiles * p->n_tiles * 4);
+        p->ws_counter_bytes = align256((size_t)p->m_tiles * p->n_tiles * 4);
         const size_t sums = p->packed ? (size_t)total_rows * N * 8 : (size_t)p->nsplit * total_rows * N * 4;
         p->ws_bytes = p->ws_counter_bytes + align256(sums);
     } else {
@@ -407,8 +421,9 @@ qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const i
     g.xq = static_cast<const uint8_t *>(xq);
     g.xs = x_scales;
     g.group_off = group_offsets;
-    g.group_mt = p.m_tiles;
-    g.m_tiles = groups * p.m_tiles;   // grid y
+    g.groups = groups;
+    g.group_rows = std::min(c.tile_m, max_group_rows);
+    g.m_tiles = p.m_tiles;   // grid y
     return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, 0, g, p.lds_bytes,
                                   static_cast<hipStream_t>(stream)));
 }

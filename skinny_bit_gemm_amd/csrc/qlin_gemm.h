@@ -244,6 +244,56 @@ __device__ __forceinline__ void reduce_slices(acc_s *part, int64_t slice, int N,
     }
 }
 
+// Inclusive prefix sum over the wave's 64 lanes through DPP (no LDS
+// traffic): shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes with
+// no source add 0), then row_bcast:15 adds row r's last sum to row r + 1
+// (rows 1 and 3) and row_bcast:31 adds lane 31's to rows 2 and 3.
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ int add_dpp(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    v = add_dpp<0x111>(v);
+    v = add_dpp<0x112>(v);
+    v = add_dpp<0x114>(v);
+    v = add_dpp<0x118>(v);
+    v = add_dpp<0x142, 0xA>(v);
+    return add_dpp<0x143, 0xC>(v);
+}
+
+// Grouped launches: finds the j-th (group, token tile) pair in the list of
+// such pairs over the groups that have rows, in group order.  Group e holds
+// rows [off[e], off[e + 1]) of `total` (clamped into range and to a
+// non-negative count) and ceil(rows / tm) tiles of tm rows.  Each wave scans
+// 64 groups at a time (one group per lane, an inclusive prefix sum of their
+// tile counts across the wave); every wave of a workgroup gets the same,
+// wave-uniform answer.  Returns false when j is past the end of the list.
+__device__ __forceinline__ bool group_tile(const int *off, int groups, int total, int tm, int j, int lane,
+                                           int &e_out, int &tile_out, int &lo_out, int &hi_out) {
+    int base = 0;
+    for (int c = 0; c < groups; c += 64) {
+        const int e = c + lane;
+        int lo = 0, hi = 0;
+        if (e < groups) {
+            lo = min(max(off[e], 0), total);
+            hi = min(max(off[e + 1], lo), total);
+        }
+        const int tiles = (hi - lo + tm - 1) / tm;
+        const int incl = wave_inclusive_sum(tiles);
+        const int sum = __builtin_amdgcn_readlane(incl, 63);
+        if (j < base + sum) {
+            const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(base + incl > j)));
+            e_out = c + l;
+            tile_out = j - base - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(tiles, l));
+            lo_out = __builtin_amdgcn_readlane(lo, l);
+            hi_out = __builtin_amdgcn_readlane(hi, l);
+            return true;
+        }
+        base += sum;
+    }
+    return false;
+}
+
 // s_waitcnt operand that waits until at most n vector memory requests are
 // outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -269,16 +319,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     const int nw = wave % g.nw, kw = wave / g.nw;
     const int TN = 16 * NR * g.nw;
     const int n_tile0 = blockIdx.x * TN;
-    // grouped launch: blockIdx.y = group * group_mt + token tile; the
-    // group's rows, weights, scales, output rows and split-K sums take the
-    // place of the call's (a group with no rows in this tile reads nothing)
-    int mtile = blockIdx.y;
+    // grouped launch: blockIdx.y is the index of a (group, token tile) pair
+    // in the list of such pairs over the groups that have rows; the group's
+    // rows, weights, scales, output rows and split-K sums take the place of
+    // the call's (workgroups past the end of the list read nothing)
+    int mtile = blockIdx.y, tile_rows = 16 * MT;
     if (g.group_off) {
-        const int e = blockIdx.y / g.group_mt;
-        mtile = blockIdx.y - e * g.group_mt;
-        const int lo = min(max(g.group_off[e], 0), g.M);
-        const int hi = min(max(g.group_off[e + 1], lo), g.M);
-        if (mtile * 16 * MT >= hi - lo) return;
+        int e, lo, hi;
+        tile_rows = g.group_rows;   // <= 16 * MT: the rows the LDS staging was sized for
+        if (!group_tile(g.group_off, g.groups, g.M, tile_rows, (int)blockIdx.y, lane, e, mtile, lo, hi)) return;
         const int Gk = (g.K + kGroup - 1) / kGroup;
         g.xq += (int64_t)lo * g.K;
         g.xs += (int64_t)lo * (FMT == FMT_BLOCK ? Gk : 1);
@@ -288,13 +337,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         if (g.acc_ws) g.acc_ws = static_cast<uint8_t *>(g.acc_ws) + (int64_t)lo * g.N * (g.packed ? 8 : 4);
         g.M = hi - lo;
     }
-    const int m0 = mtile * 16 * MT;
+    const int m0 = mtile * tile_rows;
     const int kb_begin = blockIdx.z * g.kb_per_split;
     const int kb_end = min(g.nkb, kb_begin + g.kb_per_split);
-    const int M = g.M, N = g.N, K = g.K;
+    const int R = min(tile_rows, g.M - m0);   // token rows that exist in this tile
+    // every row guard below is against the tile's own end (in a grouped
+    // launch the next rows may belong to the next tile)
+    const int M = m0 + R, N = g.N, K = g.K;
     const int r16 = lane & 15, quarter = lane >> 4;
     const int G = (K + kGroup - 1) / kGroup;
-    const int R = min(16 * MT, M - m0);   // token rows that exist in this tile
     const int RS = 8 * g.phase_blocks + 1;   // LDS staging row stride in 16-byte slots (odd)
     // fused path: the first column of workgroups also stores the codes and
     // scales it produces (every workgroup of a row of tiles produces the same)

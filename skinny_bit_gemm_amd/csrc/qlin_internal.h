@@ -42,9 +42,12 @@ struct GemmLaunch {
     int64_t slice;       // split-K slice stride in elements (M x N; total rows x N when grouped)
     // grouped launches (mixture of experts): group e's rows are
     // [group_off[e], group_off[e + 1]) of the call's M rows, its weights and
-    // scales the e-th of the call's; grid y = groups x group_mt token tiles
+    // scales the e-th of the call's; grid y covers the (group, token tile)
+    // pairs of the groups that have rows, in group order (workgroups past
+    // the last pair exit at once)
     const int *group_off;
-    int group_mt;
+    int groups;
+    int group_rows;      // rows per token tile of a grouped launch (<= tile_m)
 };
 
 // Derived launch geometry for (fmt, M, N, K, cfg).

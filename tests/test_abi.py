@@ -303,7 +303,10 @@ def test_grouped_gemm_validation():
     assert gg(out=q.QLIN_OUT_I32_ACC, total=0) == EINVAL       # int32 sums: W8A8_INT8 only
     assert gg(cfg=q.make_config(0, 1, 64, 128, 4, 1), total=0) == EINVAL   # large-M tiles: not grouped
     assert gg(cfg=q.make_config(1, 1, 16, 32, 4, 4, 0, 1), total=0) == EINVAL   # codes come quantized
-    assert gg(groups=40000, maxr=32, cfg=q.make_config(1, 1, 16, 64, 4, 2), total=0) == ESHAPE   # grid y
+    # grid y: ceil(total / tile rows) + min(groups, total) token tiles, at most 65535
+    assert gg(total=70000, maxr=1) == ESHAPE
+    assert gg(groups=50000, total=50000, maxr=2) == ESHAPE   # 25000 + 50000 tiles
+    assert q.qlin_grouped_workspace_bytes(FP8, 40000, 256, 512, 0, 32) == 0
     split = q.make_config(1, 2, 16, 64, 4, 2)
     need = q.qlin_grouped_workspace_bytes(FP8, 4, 256, 512, 9, 4, split)
     assert need > 0 and q.qlin_grouped_workspace_bytes(FP8, 4, 256, 512, 9, 4) == 0
@@ -312,3 +315,6 @@ def test_grouped_gemm_validation():
     c = q.qlin_grouped_select_variant(FP8, 128, 1536, 2048, 8)
     assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.fuse_quant) == (1, 1, 16, 64, 0)
     assert q.qlin_grouped_select_variant(I8, 128, 2048, 768, 32).tile_m == 32
+    c = q.qlin_grouped_select_variant(FP8, 128, 1536, 2048, 2)
+    assert (c.tile_n, c.waves, c.k_waves) == (32, 4, 4)
+    assert q.qlin_grouped_select_variant(FP8, 128, 2048, 768, 2).tile_n == 64

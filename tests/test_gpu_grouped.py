@@ -65,7 +65,7 @@ def run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, max_rows, c, out_type=q.QLIN_OU
     return y
 
 
-def check_case(fmt, E, N, K, T, topk, seed, c):
+def check_case(fmt, E, N, K, T, topk, seed, c, max_rows=None):
     offsets, rows = wl.moe_routing(T, E, topk, seed)
     x = wl.random_bf16((T, K), seed + 7)[rows]
     xq, xs = gpu_quant_act(fmt, x)
@@ -74,13 +74,14 @@ def check_case(fmt, E, N, K, T, topk, seed, c):
     qw, sw = experts(fmt, E, N, K, 1000 * seed)
     wqd, wsd = to_dev(qw), to_dev(sw)
     print(f"[grouped] fmt={fmt} E={E} N={N} K={K} T={T} top{topk} cfg={c}", flush=True)
-    y = run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, T, c)
+    max_rows = T if max_rows is None else max_rows
+    y = run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, max_rows, c)
     ref = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw)
     ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
     assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
     if fmt == wl.W8A8_INT8:
         _, acc = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw, want_acc=True)
-        yi = run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, T, c, q.QLIN_OUT_I32_ACC)
+        yi = run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, max_rows, c, q.QLIN_OUT_I32_ACC)
         assert np.array_equal(yi.cpu().numpy(), acc), "int32 accumulators differ"
 
 
@@ -104,6 +105,19 @@ def test_grouped_ragged_k_and_many_rows(fmt, tile_m):
     # K not a multiple of 128; 40 tokens top-2 of 4 experts: groups of 18 to
     # 25 rows, so several token tiles per group with a ragged last one
     check_case(fmt, 4, 256, 1040, 40, 2, 3, cfg(1, 1, tile_m, 64, 4, 2))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("max_rows,c", [(2, None), (5, cfg(1, 1, 16, 64, 4, 2)), (3, cfg(0, 2, 32, 32, 4, 2)),
+                                        (7, cfg(1, 2, 32, 64, 4, 2, reduce=1))],
+                         ids=["tiles_of_2", "tiles_of_5", "tiles_of_3_split2", "tiles_of_7_packed2"])
+def test_grouped_groups_larger_than_max_rows(fmt, max_rows, c):
+    """max_group_rows below the largest group (13 tokens top-2 of 3 experts:
+    groups of 6 to 11 rows): token tiles of min(tile_m, max_group_rows)
+    rows, every row still computed."""
+    if fmt == wl.BLOCK_FP8 and c is not None and c.reduce:
+        c = cfg(1, 2, 32, 64, 4, 2)
+    check_case(fmt, 3, 256, 512, 13, 2, 4, c, max_rows=max_rows)
 
 
 def test_grouped_graph_replays_follow_new_routing():

@@ -132,9 +132,10 @@ def random_weights(N: int, K: int, seed: int, std: float = 0.02) -> np.ndarray:
 
 # A mixture-of-experts layer of the 30B-class, 3B-active shape (hidden 2048,
 # 128 experts of width 768, top-8 routing): the grouped product's workload.
-# The pages name MoE layers as the next target ("Helion gives vLLM's linear
-# backend a reported 10%+ throughput lift on some workloads", section
-# "Future work"); they give no MoE shapes, so this is a representative one.
+# The pages name MoE layers as the next target ("Building a High-Performance
+# and Portable vLLM Linear Backend with Helion", section "Future work", its
+# model-coverage paragraph); they give no MoE shapes, so this is a
+# representative one.
 MOE_EXPERTS = 128
 MOE_TOPK = 8
 MOE_LAYERS = (Layer("expert_gate_up", 1536, 2048), Layer("expert_down", 2048, 768))
