@@ -324,7 +324,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     // rows, weights, scales, output rows and split-K sums take the place of
     // the call's (workgroups past the end of the list read nothing)
     int mtile = blockIdx.y, tile_rows = 16 * MT;
-    if (g.group_off) {
+    // (grouped launches take quantized codes: the fused variants leave this out)
+    if (!FUSE && g.group_off) {
         int e, lo, hi;
         tile_rows = g.group_rows;   // <= 16 * MT: the rows the LDS staging was sized for
         if (!group_tile(g.group_off, g.groups, g.M, tile_rows, (int)blockIdx.y, lane, e, mtile, lo, hi)) return;
