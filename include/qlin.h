@@ -184,7 +184,11 @@ qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qli
  *                  total_rows: group e owns rows [off[e], off[e+1]) of xq,
  *                  x_scales and y.  Read by the kernel, so a captured graph
  *                  can be replayed after the routing changes.  A group
- *                  with no rows reads none of its weights.
+ *                  with no rows reads none of its weights.  (The kernel
+ *                  clamps the offsets into [0, total_rows] and takes
+ *                  running maxima, so whatever the array holds, groups
+ *                  never overlap and nothing outside y is written; rows in
+ *                  no group are left as they were.)
  *   total_rows     rows of xq / x_scales / y (0: nothing is enqueued)
  *   max_group_rows the expected largest group: token tiles hold
  *                  min(tile_m, max_group_rows) rows.  Larger groups are

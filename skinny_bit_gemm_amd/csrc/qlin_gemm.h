@@ -244,13 +244,18 @@ __device__ __forceinline__ void reduce_slices(acc_s *part, int64_t slice, int N,
     }
 }
 
-// Inclusive prefix sum over the wave's 64 lanes through DPP (no LDS
-// traffic): shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes with
-// no source add 0), then row_bcast:15 adds row r's last sum to row r + 1
-// (rows 1 and 3) and row_bcast:31 adds lane 31's to rows 2 and 3.
-template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+// Inclusive prefix sum / maximum over the wave's 64 lanes through DPP (no
+// LDS traffic): shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes
+// with no source combine with 0), then row_bcast:15 combines row r's last
+// value into row r + 1 (rows 1 and 3) and row_bcast:31 lane 31's into rows 2
+// and 3.  (The maximum is meant for non-negative values.)
+template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ int add_dpp(int v) {
-    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int max_dpp_i(int v) {
+    return max(v, __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false));
 }
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
     v = add_dpp<0x111>(v);
@@ -260,25 +265,38 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     v = add_dpp<0x142, 0xA>(v);
     return add_dpp<0x143, 0xC>(v);
 }
+__device__ __forceinline__ int wave_inclusive_max(int v) {
+    v = max_dpp_i<0x111>(v);
+    v = max_dpp_i<0x112>(v);
+    v = max_dpp_i<0x114>(v);
+    v = max_dpp_i<0x118>(v);
+    v = max_dpp_i<0x142, 0xA>(v);
+    return max_dpp_i<0x143, 0xC>(v);
+}
 
 // Grouped launches: finds the j-th (group, token tile) pair in the list of
 // such pairs over the groups that have rows, in group order.  Group e holds
-// rows [off[e], off[e + 1]) of `total` (clamped into range and to a
-// non-negative count) and ceil(rows / tm) tiles of tm rows.  Each wave scans
-// 64 groups at a time (one group per lane, an inclusive prefix sum of their
-// tile counts across the wave); every wave of a workgroup gets the same,
-// wave-uniform answer.  Returns false when j is past the end of the list.
+// rows [P(e), P(e + 1)) of `total`, where P(x) is the largest of off[0..x]
+// clamped into [0, total]: for non-decreasing offsets that is off[e] ..
+// off[e + 1], and whatever the offsets, the groups' rows never overlap (so
+// two groups never share outputs or split-K sums).  A group has
+// ceil(rows / tm) tiles of tm rows.  Each wave scans 64 groups at a time
+// (one group per lane: running maxima of the offsets and an inclusive prefix
+// sum of the tile counts across the wave); every wave of a workgroup gets the
+// same, wave-uniform answer.  Returns false when j is past the end of the list.
 __device__ __forceinline__ bool group_tile(const int *off, int groups, int total, int tm, int j, int lane,
                                            int &e_out, int &tile_out, int &lo_out, int &hi_out) {
-    int base = 0;
+    int base = 0, carry = 0;   // tiles and P(c) of the groups before this chunk
     for (int c = 0; c < groups; c += 64) {
         const int e = c + lane;
-        int lo = 0, hi = 0;
+        int a = 0, b = 0;
         if (e < groups) {
-            lo = min(max(off[e], 0), total);
-            hi = min(max(off[e + 1], lo), total);
+            a = min(max(off[e], 0), total);
+            b = min(max(off[e + 1], 0), total);
         }
-        const int tiles = (hi - lo + tm - 1) / tm;
+        const int lo = max(carry, wave_inclusive_max(a));    // P(e)
+        const int hi = max(lo, wave_inclusive_max(b));       // P(e + 1)
+        const int tiles = e < groups ? (hi - lo + tm - 1) / tm : 0;
         const int incl = wave_inclusive_sum(tiles);
         const int sum = __builtin_amdgcn_readlane(incl, 63);
         if (j < base + sum) {
@@ -290,6 +308,7 @@ __device__ __forceinline__ bool group_tile(const int *off, int groups, int total
             return true;
         }
         base += sum;
+        carry = __builtin_amdgcn_readlane(hi, 63);
     }
     return false;
 }

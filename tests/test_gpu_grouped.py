@@ -154,19 +154,26 @@ def test_grouped_graph_replays_follow_new_routing():
         q.qlin_graph_destroy(g)
 
 
-def test_grouped_moe_layer_shape():
-    """The 128-expert top-8 layer (gate_up: 1536 x 2048) at 4 tokens, with
-    the default schedule; only the active experts' weights are quantized."""
-    fmt, E, N, K, T, topk = wl.FP8_DYNAMIC, wl.MOE_EXPERTS, 1536, 2048, 4, wl.MOE_TOPK
+@pytest.mark.parametrize("fmt,layer,T", [(f, L, 4) for f in FMTS for L in wl.MOE_LAYERS]
+                         + [(wl.W8A8_INT8, wl.MOE_LAYERS[0], 32), (wl.BLOCK_FP8, wl.MOE_LAYERS[1], 32)],
+                         ids=lambda v: v.name if isinstance(v, wl.Layer) else
+                         (wl.FORMAT_NAMES.get(v) if v in (0, 1, 2) and not isinstance(v, bool) else str(v)))
+def test_grouped_moe_layer_shape(fmt, layer, T):
+    """The 128-expert top-8 layers at their full shapes, with the default
+    schedule; only the active experts' weights are quantized (the others
+    stay zero and must not matter)."""
+    E, topk, N, K = wl.MOE_EXPERTS, wl.MOE_TOPK, layer.N, layer.K
     offsets, rows = wl.moe_routing(T, E, topk, 5)
     x = wl.activations(fmt, N, K, T)[rows]
     xq, xs = gpu_quant_act(fmt, x)
     qa, sa = oracle.quant_act(fmt, x)
     qw = np.zeros((E, N, K), dtype=np.uint8)
-    sw = np.ones((E, N), dtype=np.float32)
+    sw = np.ones((E,) + oracle.scale_shape(fmt, N, K, True), dtype=np.float32)
     active = [e for e in range(E) if offsets[e + 1] > offsets[e]]
-    for e in active:
-        qw[e], sw[e] = oracle.quant_weight(fmt, wl.random_weights(N, K, 9000 + e))
+    for e in active:   # N(0, 0.02) weights, drawn in float32 (seeded per expert)
+        w = np.random.default_rng(9000 + e).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+        qw[e], sw[e] = oracle.quant_weight(fmt, w)
+    print(f"[grouped-moe] fmt={fmt} {layer.name} T={T} active={len(active)}", flush=True)
     y = run(fmt, offsets, xq, xs, to_dev(qw), to_dev(sw), E, N, K, T, None)
     ref = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw)
     ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
