@@ -195,6 +195,12 @@ def cpu_baseline(fmt, layers, Ms, budget_s):
         if spent > 4 * budget_s:
             break
     best = min(times)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(pass_bytes / best / 1e9, 4),
         "unit": "GB/s",
@@ -204,6 +210,7 @@ def cpu_baseline(fmt, layers, Ms, budget_s):
                   f"epilogue each), best of {len(times)} timed passes after one warm-up, "
                   f"{spent:.1f} s of CPU time in total",
         "ms_per_pass": round(best * 1e3, 2),
+        "cpu_model": model,
     }
 
 
