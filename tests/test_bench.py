@@ -1,0 +1,57 @@
+"""CPU checks of bench.py's host logic: the one-GPU contract, the traffic
+record's freshness check, the CPU-oracle baseline leg and the MoE mode's
+schedule set (nothing here launches a kernel)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as wl  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_traffic_record_matches_the_sources_it_was_taken_on():
+    ksha, tsha = bench.source_digests()
+    assert len(ksha) == 64 and len(tsha) == 64
+    assert bench.source_digests() == (ksha, tsha)        # deterministic
+    path = os.path.join(ROOT, "profiles", "gemm_traffic_fp8_dynamic_hidden2048.json")
+    rec = json.load(open(path))
+    got = bench.measured_traffic("fp8_dynamic_hidden2048")
+    if rec["kernel_source_sha256"] == ksha and rec["table_sha256"] == tsha:
+        assert got is not None and got["per_launch_traffic_bytes"] > got["per_launch_algorithmic_bytes"] > 0
+    else:
+        assert got is None                               # stale records are never reported
+    assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_cpu_baseline_leg_on_the_tiny_case():
+    fmt, layers, Ms = wl.WORKLOADS["tiny_w8a8_int8"]
+    out = bench.cpu_baseline(fmt, layers, Ms, budget_s=0.2)
+    assert out["kind"] == "oracle" and out["unit"] == "GB/s"
+    assert out["value"] > 0 and out["cores"] >= 1 and out["ms_per_pass"] > 0
+    assert "linears" in out["sample"]
+
+
+def test_moe_schedules_are_valid_grouped_configs():
+    q = pytest.importorskip("skinny_bit_gemm_amd")
+    q.lib()
+    E = wl.MOE_EXPERTS
+    for fmt in (wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8):
+        for L in wl.MOE_LAYERS:
+            for T in wl.MOE_TOKENS:
+                for name, c in bench.moe_configs(q, fmt, T).items():
+                    # every forced schedule plans for the layer (no launch)
+                    assert q.qlin_grouped_workspace_bytes(fmt, E, L.N, L.K, T * wl.MOE_TOPK, T, c) >= 0, name
