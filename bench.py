@@ -84,11 +84,12 @@ class Linear:
         self.qbytes = wl.quant_bytes(fmt, M, layer.K)
         self.flops = wl.flops(M, layer.N, layer.K)
 
-    def layer(self, stream):
+    def layer(self, stream, wq=None):
         """The whole decode linear: quantize + GEMM (one or two kernels, as tuned)."""
         import skinny_bit_gemm_amd as q
-        q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, self.wq,
-                      self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work, stream=stream)
+        q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs,
+                      self.wq if wq is None else wq, self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work,
+                      stream=stream)
 
     def gemm(self, stream, wq=None):
         import skinny_bit_gemm_amd as q
@@ -99,14 +100,14 @@ class Linear:
     def fused(self):
         return bool(self.cfg.fuse_quant)
 
-    def kernel(self, stream):
+    def kernel(self, stream, wq=None):
         """The step's GEMM kernel of this linear, as the step runs it: the
         fused quantize + GEMM kernel where the table fuses them, else the
         GEMM kernel alone (its codes come from the step's quantize kernel)."""
         if self.fused:
-            self.layer(stream)
+            self.layer(stream, wq)
         else:
-            self.gemm(stream)
+            self.gemm(stream, wq)
 
     @property
     def kernel_bytes(self):
@@ -537,7 +538,8 @@ def main():
         detail = []
         if args.detail:
             # per (M, layer): graphs of the whole linear and of its GEMM
-            # kernel over every weight copy
+            # kernel over >= 1 GiB of copies of that layer's weights (fewer
+            # would leave a small layer's copies in the L2 and Infinity Cache)
             def per_launch_us(ls, fn):
                 reps = max(1, -(-64 // len(ls)))
                 g = capture(stream, lambda: [fn(l) for _ in range(reps) for l in ls])
@@ -553,10 +555,13 @@ def main():
                 return d0.elapsed_time(d1) * 1e3 / (5 * reps * len(ls))
 
             for j in range(n_gemm):
-                ls = [s_[j] for s_ in sets]
-                l0 = ls[0]
-                layer_us = per_launch_us(ls, lambda l: l.layer(stream))
-                kernel_us = per_launch_us(ls, lambda l: l.kernel(stream))
+                l0 = sets[0][j]
+                n_copies = max(2, -(-(1 << 30) // (l0.N * l0.K)))
+                copies = [s_[j].wq for s_ in sets][:n_copies]
+                copies += [l0.wq.clone() for _ in range(n_copies - len(copies))]
+                layer_us = per_launch_us(copies, lambda w: l0.layer(stream, w))
+                kernel_us = per_launch_us(copies, lambda w: l0.kernel(stream, w))
+                del copies
                 detail.append({"layer": l0.name, "M": l0.M, "N": l0.N, "K": l0.K, "fused": l0.fused,
                                "layer_us": round(layer_us, 3),
                                "layer_GBps": round((l0.bytes + l0.qbytes) / layer_us / 1e3, 1),
