@@ -189,7 +189,7 @@ def cpu_baseline(fmt, layers, Ms, budget_s):
     one_pass()                      # warm-up
     times = []
     spent = 0.0
-    while len(times) < 3 or (spent < budget_s and len(times) < 50):
+    while len(times) < 3 or (spent < budget_s and len(times) < 1000):
         t = one_pass()
         times.append(t)
         spent += t
