@@ -97,6 +97,7 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
         if (!gemm_variant_exists(fmt, c.tile_m, 0, 0)) return QLIN_ERR_INVALID_ARG;
         p->tile_m = c.tile_m;
         p->tile_n = 128;
+        p->sub_rows = 16;
         p->nr = 0;
         p->nw = 2;
         p->kw = 1;
@@ -115,11 +116,20 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
         return QLIN_OK;
     }
     const int nw = c.waves / c.k_waves;
-    if (c.tile_n < 16 || c.tile_n > 256 || c.tile_n % (16 * nw) != 0) return QLIN_ERR_INVALID_ARG;
-    const int nr = c.tile_n / (16 * nw);
+    // weight sub-tiles of 16 rows (the matrix core's), or of 8 rows where
+    // tile_n = 8 x nw: the other 8 rows of each sub-tile read zeros, which
+    // doubles the workgroups a narrow layer spreads over
+    if (c.tile_n < 8 || c.tile_n > 256) return QLIN_ERR_INVALID_ARG;
+    int sub_rows = 16;
+    if (c.tile_n % (16 * nw) != 0) {
+        if (c.tile_n != 8 * nw) return QLIN_ERR_INVALID_ARG;
+        sub_rows = 8;
+    }
+    const int nr = c.tile_n / (sub_rows * nw);
     const int mt = c.tile_m / 16;
     p->tile_m = c.tile_m;
     p->tile_n = c.tile_n;
+    p->sub_rows = sub_rows;
     p->nr = nr;
     p->nw = nw;
     p->kw = c.k_waves;
@@ -273,6 +283,7 @@ static GemmLaunch launch_args(const Plan &p, int M, int N, int K, const void *wq
     g.m_tiles = p.m_tiles;
     g.nw = p.nw;
     g.kw = p.kw;
+    g.sub_rows = p.sub_rows;
     g.slice = (int64_t)M * N;
     return g;
 }

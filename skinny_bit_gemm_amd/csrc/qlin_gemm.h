@@ -20,11 +20,14 @@ namespace qlin {
 // ---------------------------------------------------------------------------
 //
 // Work decomposition.  A workgroup owns a tile of up to TM = 16*MT tokens by
-// TN = 16*NR*nw output channels and a range of 128-wide K blocks (all of K,
+// TN = SR*NR*nw output channels and a range of 128-wide K blocks (all of K,
 // or one Split-K partition).  Its waves form an nw x kw grid: a wave owns NR
-// sub-tiles of 16 channels and every kw-th K block of the range, so the kw
+// sub-tiles of SR channels and every kw-th K block of the range, so the kw
 // waves of a column stream neighbouring K blocks of the same weight rows at
-// the same time; their partial sums are added through LDS at the end.
+// the same time; their partial sums are added through LDS at the end.  A
+// sub-tile is the matrix core's 16 rows (SR = 16), or 8 of them (SR = 8: the
+// other 8 read zeros and are never stored), which halves the weight bytes
+// per workgroup and doubles the workgroups a narrow layer spreads over.
 //
 // Operand fragments.  For one 128-wide K block a lane l (row r = l % 16,
 // quarter q = l / 16) holds 32 consecutive bytes k = 32q .. 32q+31 of its
@@ -336,7 +339,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     const int nthreads = blockDim.x;
     const int nwaves = nthreads >> 6;
     const int nw = wave % g.nw, kw = wave / g.nw;
-    const int TN = 16 * NR * g.nw;
+    // weight rows per sub-tile: 16, or 8 (then the other 8 rows of the
+    // matrix core's 16 read zeros, and their outputs are never stored)
+    const int SR = g.sub_rows;
+    const int TN = SR * NR * g.nw;
     const int n_tile0 = blockIdx.x * TN;
     // grouped launch: blockIdx.y is the index of a (group, token tile) pair
     // in the list of such pairs over the groups that have rows; the group's
@@ -365,6 +371,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     // launch the next rows may belong to the next tile)
     const int M = m0 + R, N = g.N, K = g.K;
     const int r16 = lane & 15, quarter = lane >> 4;
+    // whether this lane's output channels are real rows of its sub-tiles
+    const bool col_ok = SWAP ? 4 * quarter < SR : r16 < SR;
     const int G = (K + kGroup - 1) / kGroup;
     const int RS = 8 * g.phase_blocks + 1;   // LDS staging row stride in 16-byte slots (odd)
     // fused path: the first column of workgroups also stores the codes and
@@ -375,10 +383,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     __amdgpu_buffer_rsrc_t wrs[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        nsub[r] = n_tile0 + (nw * NR + r) * 16;
+        nsub[r] = n_tile0 + (nw * NR + r) * SR;
         // sub-tiles past N get an empty resource: their loads return zeros
-        const int base = min(nsub[r], N - 16);
-        wrs[r] = buffer_rsrc(g.wq + (int64_t)base * K, nsub[r] < N ? 16u * K : 0u);
+        // (as do rows SR .. 15 of a sub-tile: past the resource's end)
+        const int base = min(nsub[r], N - SR);
+        wrs[r] = buffer_rsrc(g.wq + (int64_t)base * K, nsub[r] < N ? (uint32_t)SR * K : 0u);
     }
     const uint32_t lane_off = (uint32_t)(r16 * K + quarter * 32);
     // the lane's activation fragment in a staged block: [half 0][quarter][row]
@@ -735,7 +744,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 if (SWAP) {
                     const int m = m0 + mt * 16 + r16;
                     const int n = nsub[r] + 4 * quarter;
-                    if (m >= M) continue;
+                    if (m >= M || !col_ok) continue;
                     if (g.out_type == QLIN_OUT_I32_ACC) {
                         *reinterpret_cast<int4 *>(static_cast<int *>(g.y) + (int64_t)m * N + n) =
                             make_int4((int)acc[r][mt][0], (int)acc[r][mt][1], (int)acc[r][mt][2],
@@ -758,7 +767,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int m = m0 + mt * 16 + 4 * quarter + i;
-                        if (m >= M) continue;
+                        if (m >= M || !col_ok) continue;
                         store1((int64_t)m * N + n, scaled((float)acc[r][mt][i], r, mt, i), (int)acc[r][mt][i]);
                     }
                 }
@@ -802,7 +811,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                         const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
                         if constexpr (FMT == FMT_I8) val[r][i] = (long long)acc[r][mt][i];
                         else val[r][i] = (long long)(acc[r][mt][i] * 262144.0f);
-                        live[r][i] = m < M && nsub[r] < N;
+                        live[r][i] = m < M && nsub[r] < N && col_ok;
                         add[r][i] = (unsigned long long)(val[r][i] + (long long)kUnit);
                         // (kept in a register of its own: formed inside the
                         // masked branch, every addend would reuse one
@@ -825,7 +834,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                     for (int i = 0; i < 4; ++i) {
                         const int m = token_of(mt, i);
                         const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
-                        if (m >= M) continue;
+                        if (m >= M || !col_ok) continue;
                         const int64_t idx = (int64_t)m * N + n;
                         const unsigned long long before = (old[r][i] + kHalf) >> 52;
                         if (before != (unsigned long long)(g.nsplit - 1)) continue;
@@ -860,7 +869,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 for (int i = 0; i < 4; ++i) {
                     const int m = token_of(mt, i);
                     const int n = SWAP ? nsub[r] + 4 * quarter + i : nsub[r] + r16;
-                    if (m < M)
+                    if (m < M && col_ok)
                         __hip_atomic_store(&part[blockIdx.z * slice + (int64_t)m * N + n],
                                            (acc_s)acc[r][mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -876,7 +885,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     }
     __syncthreads();
     if (!s_last) return;
-    const int tn = min(TN, N - n_tile0);   // a multiple of 16
+    const int tn = min(TN, N - n_tile0);   // a multiple of 8
     reduce_slices(part, slice, N, m0, n_tile0, R, tn, g.nsplit, (int)threadIdx.x, nthreads,
                   [&](int m, int n, const acc_s (&v)[4]) {
 #pragma unroll

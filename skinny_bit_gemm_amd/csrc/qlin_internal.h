@@ -45,6 +45,7 @@ struct GemmLaunch {
     // scales the e-th of the call's; grid y covers the (group, token tile)
     // pairs of the groups that have rows, in group order (workgroups past
     // the last pair exit at once)
+    int sub_rows;        // weight rows per 16-row sub-tile that are real (16, or 8)
     const int *group_off;
     int groups;
     int group_rows;      // rows per token tile of a grouped launch (<= tile_m)
@@ -53,6 +54,7 @@ struct GemmLaunch {
 // Derived launch geometry for (fmt, M, N, K, cfg).
 struct Plan {
     int tile_m, tile_n, nr, nw, kw, waves;
+    int sub_rows;         // weight rows per sub-tile: 16, or 8 (tile_n = 8 x nw)
     int nkb, kb_per_split, nsplit, phase_blocks;
     int n_tiles, m_tiles;
     size_t lds_bytes;

@@ -91,10 +91,15 @@ def test_gemm_rejects_bad_configs():
            q.make_config(tile_m=8), q.make_config(waves=3, k_waves=1),
            q.make_config(waves=4, k_waves=3), q.make_config(tile_n=24, waves=1, k_waves=1),
            q.make_config(tile_n=512, waves=1, k_waves=1),
-           q.make_config(tile_n=32, waves=4, k_waves=1)]   # 4 column waves need tile_n >= 64
+           q.make_config(tile_n=16, waves=4, k_waves=1),   # 4 column waves need tile_n >= 32
+           q.make_config(tile_n=48, waves=4, k_waves=1)]   # neither 16-row nor 8-row sub-tiles
     for c in bad:
         assert gemm(cfg=c) == EINVAL, c
         assert q.qlin_validate_config(FP8, 4, 256, 512, c) == EINVAL
+    # 8-row weight sub-tiles: tile_n = 8 x (column waves)
+    for c in (q.make_config(tile_n=8, waves=1, k_waves=1), q.make_config(tile_n=8, waves=4, k_waves=4),
+              q.make_config(tile_n=16, waves=2, k_waves=1), q.make_config(tile_n=32, waves=4, k_waves=1)):
+        assert q.qlin_validate_config(FP8, 4, 256, 512, c) == OK, c
 
 
 def test_large_m_configs():

@@ -41,8 +41,11 @@ SCHEDULES = {
     "std_nw4": cfg(0, 1, 16, 128, 8, 2),
     "split2": cfg(1, 2, 16, 64, 4, 2),
     "split3_std": cfg(0, 3, 32, 32, 4, 4),
+    "half8": cfg(1, 1, 16, 8, 4, 4),
+    "half16_std_split2": cfg(0, 2, 16, 16, 2, 1),
 }
-PACKED = {"packed2": cfg(1, 2, 16, 64, 4, 2, reduce=1), "packed4_std": cfg(0, 4, 16, 32, 4, 2, reduce=1)}
+PACKED = {"packed2": cfg(1, 2, 16, 64, 4, 2, reduce=1), "packed4_std": cfg(0, 4, 16, 32, 4, 2, reduce=1),
+          "packed2_half8": cfg(1, 2, 16, 8, 2, 2, reduce=1)}
 
 
 def experts(fmt, E, N, K, seed):

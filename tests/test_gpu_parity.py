@@ -46,6 +46,11 @@ SCHEDULES = {
     "nw4": cfg(0, 3, 16, 128, 8, 2),
     "nr4": cfg(1, 2, 32, 64, 1, 1),
     "w8k8": cfg(0, 1, 16, 16, 8, 8),
+    # 8-row weight sub-tiles (tile_n = 8 x column waves)
+    "half8_swap": cfg(1, 1, 16, 8, 1, 1),
+    "half8_std_kw4": cfg(0, 1, 16, 8, 4, 4),
+    "half16_nw2_split3": cfg(0, 3, 32, 16, 2, 1),
+    "half32_nw4_swap_split2": cfg(1, 2, 32, 32, 4, 1),
     # the large-M kernel: 64- or 128-token tiles of 128 channels, 4 waves
     "big64": cfg(0, 1, 64, 128, 4, 1),
     "big128_split3": cfg(0, 3, 128, 128, 4, 1),
@@ -55,6 +60,8 @@ PACKED = {
     "packed4_swap": cfg(1, 4, 16, 64, 4, 1, reduce=1),
     "packed16": cfg(1, 16, 32, 16, 2, 2, reduce=1),
     "packed3_nw4": cfg(0, 3, 16, 128, 8, 2, reduce=1),
+    "packed2_half8_swap": cfg(1, 2, 16, 8, 2, 2, reduce=1),
+    "packed3_half16_std": cfg(0, 3, 32, 16, 2, 1, reduce=1),
 }
 
 
@@ -138,6 +145,8 @@ LAYER_CFGS = {
     "fused_split_std": cfg(0, 3, 16, 16, 8, 8, fuse=1),
     "fused_nr4": cfg(1, 2, 16, 256, 8, 2, fuse=1),
     "unfused": cfg(1, 2, 16, 32, 4, 4),
+    "fused_half8": cfg(1, 1, 16, 8, 8, 8, fuse=1),
+    "fused_half16_std_split2": cfg(0, 2, 16, 16, 8, 4, fuse=1),
     "unfused_m32": cfg(0, 2, 32, 64, 4, 2),
 }
 
@@ -231,6 +240,18 @@ def test_ragged_k(fmt, K):
     w = wl.random_weights(N, K, K + 1)
     for sched in ("std", "swap", "splitk2", "splitk16", "nw4", "big64", "big128_split3"):
         check_linear(fmt, M, N, K, x, w, sched, "ragged K")
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
+def test_half_sub_tiles_ragged_n(fmt):
+    """8-row weight sub-tiles with N = 368 = 11.5 tiles of 32: the last
+    workgroup has two real sub-tiles and two past N; every schedule family."""
+    M, N, K = 5, 368, 1024 + 16
+    x = wl.random_bf16((M, K), 8)
+    w = wl.random_weights(N, K, 9)
+    for c in (cfg(1, 1, 16, 32, 4, 1), cfg(0, 1, 16, 32, 4, 1), cfg(1, 3, 16, 32, 4, 1),
+              cfg(0, 2, 16, 32, 4, 1, reduce=1), cfg(1, 1, 16, 8, 2, 2)):
+        check_linear(fmt, M, N, K, x, w, c, "half sub-tiles, ragged N")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
