@@ -31,10 +31,13 @@ FMT_NAMES = {q.QLIN_FP8_DYNAMIC: "fp8_dynamic", q.QLIN_W8A8_INT8: "w8a8_int8",
              q.QLIN_BLOCK_FP8: "block_fp8"}
 FMT_IDS = {v: k for k, v in FMT_NAMES.items()}
 
-# (tile_n, waves, k_waves)
+# (tile_n, waves, k_waves); tile_n = 8 x (waves / k_waves) selects 8-row
+# weight sub-tiles
 TILES = [(16, 1, 1), (16, 2, 2), (16, 4, 4), (16, 8, 8), (32, 1, 1), (32, 2, 2), (32, 4, 4),
          (32, 4, 2), (32, 8, 8), (32, 8, 4), (64, 1, 1), (64, 2, 1), (64, 4, 4), (64, 4, 2),
-         (64, 4, 1), (64, 8, 4), (64, 8, 2), (128, 4, 1), (128, 8, 2), (128, 8, 1)]
+         (64, 4, 1), (64, 8, 4), (64, 8, 2), (128, 4, 1), (128, 8, 2), (128, 8, 1),
+         (8, 1, 1), (8, 2, 2), (8, 4, 4), (8, 8, 8), (16, 2, 1), (16, 4, 2), (16, 8, 4), (32, 4, 1),
+         (32, 8, 2), (64, 8, 1)]
 SPLITS = [1, 2, 3, 4, 6, 8, 12, 16, 24, 32]
 
 
