@@ -142,7 +142,7 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off)
 }
 
 // 32 bytes of the lane's weight row in K block kb (lane_off = row * K + 32 *
-// quarter, in a resource that covers one 16-row sub-tile; k = the lane's
+// quarter, in a resource that covers one sub-tile of 16 or 8 rows; k = the lane's
 // first K index).  The block's offset is a scalar operand, so a slot costs
 // no address registers.  A 16-byte half at or past K (in a partial last
 // block), or a dead slot, uses an out-of-range lane offset, so every lane
