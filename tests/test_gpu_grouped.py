@@ -157,10 +157,12 @@ def test_grouped_graph_replays_follow_new_routing():
         q.qlin_graph_destroy(g)
 
 
-@pytest.mark.parametrize("fmt,layer,T", [(f, L, 4) for f in FMTS for L in wl.MOE_LAYERS]
-                         + [(wl.W8A8_INT8, wl.MOE_LAYERS[0], 32), (wl.BLOCK_FP8, wl.MOE_LAYERS[1], 32)],
-                         ids=lambda v: v.name if isinstance(v, wl.Layer) else
-                         (wl.FORMAT_NAMES.get(v) if v in (0, 1, 2) and not isinstance(v, bool) else str(v)))
+MOE_CASES = [(f, L, 4) for f in FMTS for L in wl.MOE_LAYERS] + [(wl.W8A8_INT8, wl.MOE_LAYERS[0], 32),
+                                                                (wl.BLOCK_FP8, wl.MOE_LAYERS[1], 32)]
+
+
+@pytest.mark.parametrize("fmt,layer,T", MOE_CASES,
+                         ids=[f"{wl.FORMAT_NAMES[f]}-{L.name}-T{T}" for f, L, T in MOE_CASES])
 def test_grouped_moe_layer_shape(fmt, layer, T):
     """The 128-expert top-8 layers at their full shapes, with the default
     schedule; only the active experts' weights are quantized (the others
