@@ -1,0 +1,35 @@
+"""CPU checks of the offline tuner's host logic: which schedule a merge keeps,
+and that tables round-trip (entries and notes) into a file the library loads."""
+import os
+
+import skinny_bit_gemm_amd as q
+from skinny_bit_gemm_amd import tune
+
+
+def test_merge_keeps_the_existing_entry_unless_clearly_beaten():
+    a, b = q.make_config(1, 1, 16, 16, 4, 4), q.make_config(1, 1, 16, 8, 4, 4)
+    # within the margin: the existing entry stays
+    assert tune.keep_or_replace(9.9, b, 10.0, a, 0.02) == (10.0, a, True)
+    assert tune.keep_or_replace(9.81, b, 10.0, a, 0.02) == (10.0, a, True)
+    # faster by more than the margin: replaced
+    assert tune.keep_or_replace(9.7, b, 10.0, a, 0.02) == (9.7, b, False)
+    # slower: kept
+    assert tune.keep_or_replace(10.5, b, 10.0, a, 0.02) == (10.0, a, True)
+    # nothing to keep
+    assert tune.keep_or_replace(9.9, b, None, None, 0.02) == (9.9, b, False)
+    # margin 0: any improvement wins
+    assert tune.keep_or_replace(9.99, b, 10.0, a, 0.0) == (9.99, b, False)
+
+
+def test_table_round_trip_keeps_entries_and_notes(tmp_path):
+    entries, notes = tune.read_entries(q.TABLE_PATH)
+    assert len(entries) >= 200 and all(len(v) == 8 for v in entries.values())
+    out = os.path.join(str(tmp_path), "t.tbl")
+    tune.write_entries(out, entries, notes)
+    again, notes2 = tune.read_entries(out)
+    assert again == entries and notes2 == notes
+    try:
+        assert q.qlin_load_table(out, raise_on_error=False) == 0
+        assert q.qlin_table_entries() == len(entries)
+    finally:
+        q.qlin_load_table(q.TABLE_PATH)
