@@ -88,11 +88,14 @@ typedef enum {
  *              (the large-M kernel for token counts past the skinny range:
  *              it needs tile_n 128, waves 4, k_waves 1, swap_ab 0,
  *              reduce 0, fuse_quant 0).
- *   tile_n     output channels per workgroup, <= 256: a multiple of 16 x
- *              (waves / k_waves) (16-row weight sub-tiles, the matrix
+ *   tile_n     output channels per workgroup, <= 256: 1, 2 or 4 times
+ *              16 x (waves / k_waves) (16-row weight sub-tiles, the matrix
  *              core's), or exactly 8 x (waves / k_waves) (8-row sub-tiles:
  *              twice the workgroups for the same layer).
- *   waves      64-lane waves per workgroup: 1, 2, 4 or 8.
+ *   waves      64-lane waves per workgroup: 1 to 8.  Column-wave counts
+ *              (waves / k_waves) of 3, 5, 6 or 7 give tile widths such as
+ *              24, 48, 96 or 224 that split a layer's N into about one tile
+ *              per compute unit.
  *   k_waves    how many of those waves split the workgroup's K range
  *              (the rest split tile_n); divides waves.
  *   reduce     how Split-K partitions are combined: 0 = every partition

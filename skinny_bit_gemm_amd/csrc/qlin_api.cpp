@@ -78,7 +78,7 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     if (c.swap_ab != 0 && c.swap_ab != 1) return QLIN_ERR_INVALID_ARG;
     if (c.split_k < 1 || c.split_k > kMaxSplit) return QLIN_ERR_INVALID_ARG;
     if (c.tile_m != 16 && c.tile_m != 32 && c.tile_m != 64 && c.tile_m != 128) return QLIN_ERR_INVALID_ARG;
-    if (c.waves != 1 && c.waves != 2 && c.waves != 4 && c.waves != 8) return QLIN_ERR_INVALID_ARG;
+    if (c.waves < 1 || c.waves > kMaxWaves) return QLIN_ERR_INVALID_ARG;
     if (c.k_waves < 1 || c.k_waves > c.waves || c.waves % c.k_waves != 0) return QLIN_ERR_INVALID_ARG;
     if (c.reduce != 0 && c.reduce != 1) return QLIN_ERR_INVALID_ARG;
     if (c.fuse_quant != 0 && c.fuse_quant != 1) return QLIN_ERR_INVALID_ARG;

@@ -37,12 +37,17 @@ FMT_NAMES = {q.QLIN_FP8_DYNAMIC: "fp8_dynamic", q.QLIN_W8A8_INT8: "w8a8_int8",
 FMT_IDS = {v: k for k, v in FMT_NAMES.items()}
 
 # (tile_n, waves, k_waves); tile_n = 8 x (waves / k_waves) selects 8-row
-# weight sub-tiles
+# weight sub-tiles.  The last group has 3, 5, 6 or 7 column waves: widths such
+# as 24, 48 or 96 rows split N = 6144, 12288 or 24576 into exactly 256 tiles
+# (one per compute unit), and 224 rows split N = 51200 into 229, where
+# power-of-two widths leave part of the chip idle for a second round.
 TILES = [(16, 1, 1), (16, 2, 2), (16, 4, 4), (16, 8, 8), (32, 1, 1), (32, 2, 2), (32, 4, 4),
          (32, 4, 2), (32, 8, 8), (32, 8, 4), (64, 1, 1), (64, 2, 1), (64, 4, 4), (64, 4, 2),
          (64, 4, 1), (64, 8, 4), (64, 8, 2), (128, 4, 1), (128, 8, 2), (128, 8, 1),
          (8, 1, 1), (8, 2, 2), (8, 4, 4), (8, 8, 8), (16, 2, 1), (16, 4, 2), (16, 8, 4), (32, 4, 1),
-         (32, 8, 2), (64, 8, 1)]
+         (32, 8, 2), (64, 8, 1),
+         (24, 3, 1), (24, 6, 2), (48, 3, 1), (48, 6, 2), (96, 3, 1), (96, 6, 2), (40, 5, 1),
+         (80, 5, 1), (48, 6, 1), (96, 6, 1), (56, 7, 1), (112, 7, 1), (224, 7, 1)]
 SPLITS = [1, 2, 3, 4, 6, 8, 12, 16, 24, 32]
 
 

@@ -88,17 +88,28 @@ def test_gemm_rejects_bad_arguments():
 
 def test_gemm_rejects_bad_configs():
     bad = [q.make_config(swap_ab=2), q.make_config(split_k=0), q.make_config(split_k=65),
-           q.make_config(tile_m=8), q.make_config(waves=3, k_waves=1),
+           q.make_config(tile_m=8), q.make_config(waves=0, k_waves=1),
+           q.make_config(waves=9, k_waves=1), q.make_config(waves=16, k_waves=16),
            q.make_config(waves=4, k_waves=3), q.make_config(tile_n=24, waves=1, k_waves=1),
            q.make_config(tile_n=512, waves=1, k_waves=1),
            q.make_config(tile_n=16, waves=4, k_waves=1),   # 4 column waves need tile_n >= 32
-           q.make_config(tile_n=48, waves=4, k_waves=1)]   # neither 16-row nor 8-row sub-tiles
+           q.make_config(tile_n=48, waves=4, k_waves=1),   # neither 16-row nor 8-row sub-tiles
+           q.make_config(tile_n=48, waves=1, k_waves=1),   # 3 sub-tiles per wave: not built
+           q.make_config(tile_n=32, waves=3, k_waves=1),   # 3 column waves: 24, 48, 96 or 192
+           q.make_config(tile_n=64, waves=6, k_waves=2)]
     for c in bad:
         assert gemm(cfg=c) == EINVAL, c
         assert q.qlin_validate_config(FP8, 4, 256, 512, c) == EINVAL
     # 8-row weight sub-tiles: tile_n = 8 x (column waves)
     for c in (q.make_config(tile_n=8, waves=1, k_waves=1), q.make_config(tile_n=8, waves=4, k_waves=4),
               q.make_config(tile_n=16, waves=2, k_waves=1), q.make_config(tile_n=32, waves=4, k_waves=1)):
+        assert q.qlin_validate_config(FP8, 4, 256, 512, c) == OK, c
+    # column-wave counts that are not powers of two
+    for c in (q.make_config(tile_n=24, waves=3, k_waves=1), q.make_config(tile_n=24, waves=6, k_waves=2),
+              q.make_config(tile_n=48, waves=3, k_waves=1), q.make_config(tile_n=96, waves=6, k_waves=2),
+              q.make_config(tile_n=96, waves=6, k_waves=1), q.make_config(tile_n=40, waves=5, k_waves=1),
+              q.make_config(tile_n=80, waves=5, k_waves=1), q.make_config(tile_n=224, waves=7, k_waves=1),
+              q.make_config(tile_n=56, waves=7, k_waves=1, fuse_quant=1)):
         assert q.qlin_validate_config(FP8, 4, 256, 512, c) == OK, c
 
 

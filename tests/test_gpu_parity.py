@@ -51,6 +51,13 @@ SCHEDULES = {
     "half8_std_kw4": cfg(0, 1, 16, 8, 4, 4),
     "half16_nw2_split3": cfg(0, 3, 32, 16, 2, 1),
     "half32_nw4_swap_split2": cfg(1, 2, 32, 32, 4, 1),
+    # column-wave counts that are not powers of two (N = 512 leaves a
+    # partial last tile for each width)
+    "odd3_swap": cfg(1, 1, 16, 48, 3, 1),
+    "odd6_std_kw2_m32": cfg(0, 1, 32, 96, 6, 2),
+    "odd5_half_swap_split2": cfg(1, 2, 16, 40, 5, 1),
+    "odd7_std_split3": cfg(0, 3, 16, 224, 7, 1),
+    "odd3_half_std_kw2_m32": cfg(0, 1, 32, 24, 6, 2),
     # the large-M kernel: 64- or 128-token tiles of 128 channels, 4 waves
     "big64": cfg(0, 1, 64, 128, 4, 1),
     "big128_split3": cfg(0, 3, 128, 128, 4, 1),
@@ -62,6 +69,8 @@ PACKED = {
     "packed3_nw4": cfg(0, 3, 16, 128, 8, 2, reduce=1),
     "packed2_half8_swap": cfg(1, 2, 16, 8, 2, 2, reduce=1),
     "packed3_half16_std": cfg(0, 3, 32, 16, 2, 1, reduce=1),
+    "packed2_odd6_swap": cfg(1, 2, 16, 96, 6, 2, reduce=1),
+    "packed3_odd7_half_std": cfg(0, 3, 32, 56, 7, 1, reduce=1),
 }
 
 
@@ -252,6 +261,42 @@ def test_half_sub_tiles_ragged_n(fmt):
     for c in (cfg(1, 1, 16, 32, 4, 1), cfg(0, 1, 16, 32, 4, 1), cfg(1, 3, 16, 32, 4, 1),
               cfg(0, 2, 16, 32, 4, 1, reduce=1), cfg(1, 1, 16, 8, 2, 2)):
         check_linear(fmt, M, N, K, x, w, c, "half sub-tiles, ragged N")
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
+def test_odd_column_waves_ragged_n(fmt):
+    """3, 5, 6 and 7 column waves with N = 368: the last workgroup holds
+    a partial tile (16- and 8-row sub-tiles, both roles, both reductions)."""
+    M, N, K = 6, 368, 1024 + 16
+    x = wl.random_bf16((M, K), 12)
+    w = wl.random_weights(N, K, 13)
+    for c in (cfg(1, 1, 16, 48, 3, 1), cfg(0, 2, 16, 40, 5, 1), cfg(1, 1, 32, 224, 7, 1),
+              cfg(0, 1, 16, 24, 3, 1), cfg(1, 3, 16, 96, 6, 2), cfg(0, 2, 16, 112, 7, 1, reduce=1)):
+        check_linear(fmt, M, N, K, x, w, c, "odd column waves, ragged N")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_linear_fused_odd_column_waves(fmt):
+    """In-kernel quantization with 192, 320, 384 and 448 threads: the row
+    chunks are spread over a thread count that is not a power of two.  At
+    K = 1536 (192 chunks of 8 values per row) 3 waves hold 8 rows in their 8
+    register chunks per thread, 5 waves 13; 6 and 7 waves hold the whole
+    16-row tile.  (The block format quantizes only the split's K range: with
+    two splits, 5 waves hold the whole tile too.)  The largest token count
+    each one holds is checked, and the next one is rejected."""
+    N, K = 512, 1536
+    for c, ms, too_many in ((cfg(1, 1, 16, 24, 3, 1, fuse=1), (1, 8), 9),
+                            (cfg(0, 2, 16, 40, 5, 1, fuse=1), (2, 13), None if fmt == wl.BLOCK_FP8 else 14),
+                            (cfg(1, 1, 16, 48, 6, 2, fuse=1), (3, 16), None),
+                            (cfg(0, 1, 16, 56, 7, 1, fuse=1), (5, 16), None),
+                            (cfg(1, 3, 16, 224, 7, 1, fuse=1), (1, 23), None)):
+        for M in ms:
+            assert q.qlin_validate_config(fmt, M, N, K, c) == 0, (c, M)
+            x = wl.activations(fmt, N, K, M)
+            w = wl.random_weights(N, K, 70 + M)
+            check_layer(fmt, M, N, K, x, w, c)
+        if too_many is not None:
+            assert q.qlin_validate_config(fmt, too_many, N, K, c) != 0, (c, too_many)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
