@@ -238,6 +238,7 @@ def crossover_sweep(path, fmts, Ms):
     as a hipGraph of launches over >= 1 GiB of rotating weight copies."""
     import torch
     import skinny_bit_gemm_amd as q
+    from skinny_bit_gemm_amd.tune import warm_graph
     import workloads as wl
     dev = torch.device("cuda:0")
     q.lib()
@@ -268,7 +269,7 @@ def crossover_sweep(path, fmts, Ms):
                                                    stream=st) for wc in copies]
                         run()
                         g = capture(st, run)
-                        q.qlin_graph_launch(g, st)
+                        warm_graph(g, st)
                         e0 = torch.cuda.Event(enable_timing=True)
                         e1 = torch.cuda.Event(enable_timing=True)
                         e0.record(st)
@@ -324,6 +325,7 @@ def moe_bench(path, fmts, Ts, layers=None, schedules=None):
     import numpy as np
     import torch
     import skinny_bit_gemm_amd as q
+    from skinny_bit_gemm_amd.tune import warm_graph
     import workloads as wl
     dev = torch.device("cuda:0")
     q.lib()
@@ -334,7 +336,7 @@ def moe_bench(path, fmts, Ts, layers=None, schedules=None):
     def timed(fn, n):
         fn()
         g = capture(st, fn)
-        q.qlin_graph_launch(g, st)
+        warm_graph(g, st)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(st)
@@ -438,6 +440,7 @@ def main():
     import torch
 
     import skinny_bit_gemm_amd as q
+    from skinny_bit_gemm_amd.tune import warm_graph
     import workloads as wl
 
     if args.workload not in wl.WORKLOADS:
@@ -543,7 +546,7 @@ def main():
             def per_launch_us(ls, fn):
                 reps = max(1, -(-64 // len(ls)))
                 g = capture(stream, lambda: [fn(l) for _ in range(reps) for l in ls])
-                q.qlin_graph_launch(g, stream)
+                warm_graph(g, stream)
                 d0 = torch.cuda.Event(enable_timing=True)
                 d1 = torch.cuda.Event(enable_timing=True)
                 d0.record(stream)

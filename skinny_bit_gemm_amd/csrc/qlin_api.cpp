@@ -347,12 +347,22 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
 // Built-in rule for grouped launches.  The groups already give the grid
 // many workgroups (active groups x channel tiles), so no split: 16- or
 // 32-token tiles (the largest group decides), Swap-AB, 64-column tiles of
-// four waves with two K waves; with at most 2 rows per group and K >= 2048,
-// 32-column tiles with four K waves (twice the workgroups, each wave's K
-// range halved), which measured ~10% faster on 128-expert layers.
+// four waves with two K waves.  Three cases differ, all measured on the
+// 128-expert layers:
+// - at most 2 rows per group and K >= 2048: 32-column tiles with four K
+//   waves (twice the workgroups, each wave's K range halved), ~10% faster;
+// - more than 2 rows per group and K <= 1024: 48-column tiles of three
+//   waves, each with the whole K range (a short K split over waves leaves
+//   each wave a few blocks and adds a reduction), 15-20% faster on
+//   768-deep rows from 32 tokens on, a few % for the block format;
+// - 32-token tiles on longer rows: Standard operand roles, 2-7% faster at
+//   24-32 tokens.
 static void grouped_default_config(int max_group_rows, int K, qlin_config *c) {
+    const int tm = max_group_rows <= 16 ? 16 : 32;
     if (max_group_rows <= 2 && K >= 2048) *c = qlin_config{1, 1, 16, 32, 4, 4, 0, 0};
-    else *c = qlin_config{1, 1, max_group_rows <= 16 ? 16 : 32, 64, 4, 2, 0, 0};
+    else if (max_group_rows > 2 && K <= 1024) *c = qlin_config{1, 1, tm, 48, 3, 1, 0, 0};
+    else if (tm == 32) *c = qlin_config{0, 1, 32, 64, 4, 2, 0, 0};
+    else *c = qlin_config{1, 1, 16, 64, 4, 2, 0, 0};
 }
 
 // Token tiles of a grouped launch: tiles of min(tile_m, max_group_rows)

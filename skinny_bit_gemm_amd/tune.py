@@ -104,6 +104,23 @@ def variants(fmt, M, N, K, c):
     return out
 
 
+def warm_graph(graph, stream, min_ms=20.0):
+    """Replays a captured graph, untimed, for about min_ms (at most 1000
+    replays).  After host-side set-up has left the GPU idle, a measurement
+    started at once ran up to ~10 % slower (5 ms of replays still left
+    3-6 %)."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    q.qlin_graph_launch(graph, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    once = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(min(1000, int(min_ms / once))):
+        q.qlin_graph_launch(graph, stream)
+
+
 class Bench:
     """Device buffers for timing one (fmt, M, N, K) linear layer."""
 
@@ -129,6 +146,7 @@ class Bench:
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         self.stream = torch.cuda.Stream()
         self.work = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+        self.warm = False
 
     def _call(self, cfg, w, st):
         q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, w, self.ws,
@@ -149,7 +167,11 @@ class Bench:
                     self._call(cfg, w, st)
             finally:
                 gr = q.qlin_graph_end(st)
-            q.qlin_graph_launch(gr, st)
+            if self.warm:
+                q.qlin_graph_launch(gr, st)
+            else:   # the first timing after the buffers were set up
+                warm_graph(gr, st)
+                self.warm = True
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(st)

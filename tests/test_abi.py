@@ -334,3 +334,12 @@ def test_grouped_gemm_validation():
     c = q.qlin_grouped_select_variant(FP8, 128, 1536, 2048, 2)
     assert (c.tile_n, c.waves, c.k_waves) == (32, 4, 4)
     assert q.qlin_grouped_select_variant(FP8, 128, 2048, 768, 2).tile_n == 64
+    # short rows with more than 2 rows per group: 48-column tiles of 3 waves, whole K per wave
+    for fmt, T in ((FP8, 3), (I8, 32), (BLK, 512)):
+        c = q.qlin_grouped_select_variant(fmt, 128, 2048, 768, T)
+        assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves) == (1, 1, 16 if T <= 16 else 32,
+                                                                                    48, 3, 1)
+    # 32-token tiles on longer rows: Standard roles
+    for K in (1152, 2048):
+        c = q.qlin_grouped_select_variant(FP8, 128, 1536, K, 32)
+        assert (c.swap_ab, c.tile_m, c.tile_n, c.waves, c.k_waves) == (0, 32, 64, 4, 2)

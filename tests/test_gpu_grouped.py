@@ -43,9 +43,12 @@ SCHEDULES = {
     "split3_std": cfg(0, 3, 32, 32, 4, 4),
     "half8": cfg(1, 1, 16, 8, 4, 4),
     "half16_std_split2": cfg(0, 2, 16, 16, 2, 1),
+    "odd48_w3": cfg(1, 1, 16, 48, 3, 1),
+    "odd96_w6kw2_std_m32": cfg(0, 1, 32, 96, 6, 2),
+    "odd40_w5_split2": cfg(1, 2, 16, 40, 5, 1),
 }
 PACKED = {"packed2": cfg(1, 2, 16, 64, 4, 2, reduce=1), "packed4_std": cfg(0, 4, 16, 32, 4, 2, reduce=1),
-          "packed2_half8": cfg(1, 2, 16, 8, 2, 2, reduce=1)}
+          "packed2_half8": cfg(1, 2, 16, 8, 2, 2, reduce=1), "packed3_odd56_w7": cfg(1, 3, 16, 56, 7, 1, reduce=1)}
 
 
 def experts(fmt, E, N, K, seed):
