@@ -16,5 +16,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def orc():
     import oracle
-    oracle.build()
+    mutant = os.environ.get("QLIN_ORACLE_MUTANT_LIB")
+    if mutant:
+        # a copy of the oracle with one mistake planted on purpose
+        # (test_oracle_mutants.py): load it instead, and never rebuild over it
+        oracle._LIB_PATH = mutant
+        oracle._lib = None
+        oracle.build = lambda force=False: mutant
+    else:
+        oracle.build()
     return oracle

@@ -196,3 +196,65 @@ def test_nonfinite_input_is_rejected(orc):
     x[0, 5] = 0x7F80    # +inf
     with pytest.raises(ValueError):
         orc.quant_act(wl.W8A8_INT8, x)
+
+
+def _f32_nearest(fr):
+    """The float32 nearest to a positive rational in float32's normal range
+    (ties to the even significand), as an exact Fraction."""
+    from fractions import Fraction
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    if Fraction(2) ** e > fr:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= fr:
+        e += 1
+    assert -126 <= e <= 127, "outside float32's normal range"
+    unit = Fraction(2) ** (e - 23)             # spacing of 24-bit significands in [2^e, 2^(e+1))
+    n, rem = divmod(fr, unit)
+    n = int(n)
+    if rem * 2 > unit or (rem * 2 == unit and n % 2 == 1):
+        n += 1
+    return n * unit
+
+
+def test_codes_come_from_the_ieee_quotient(orc):
+    """A code is formed from x / s rounded once to float32, not from x times
+    a rounded 1/s.  The two differ in the last bit of the quotient now and
+    then, and where that decides a code (a quotient at an int8 tie, or at an
+    e4m3 midpoint) the oracle must give the code of the correctly rounded
+    quotient, computed here in exact rational arithmetic.  The pairs come
+    from a search over bf16 values for those where the two quotients give
+    different codes; both formats must meet at least 20 of them."""
+    from fractions import Fraction
+    bf = (np.arange(0x0080, 0x7F80, dtype=np.uint32) << 16).view(np.float32)   # positive normal bf16
+    rng = np.random.default_rng(1)
+    amaxes = rng.choice(bf[(bf > 1e-3) & (bf < 1e3)], 300, replace=False)
+    checked = {wl.W8A8_INT8: 0, wl.FP8_DYNAMIC: 0}
+    for fmt in checked:
+        qmax = np.float32(QMAX[fmt])
+        for a in amaxes:
+            s = np.float32(a) / qmax
+            xs = bf[bf <= a]
+            qd, qr = xs / s, xs * (np.float32(1.0) / s)
+            if fmt == wl.W8A8_INT8:
+                sel = np.rint(qd) != np.rint(qr)
+            else:
+                sel = orc.e4m3_encode(qd) != orc.e4m3_encode(qr)
+            if not sel.any():
+                continue
+            xsel = xs[sel][:8]
+            row = _f32_to_bf16_exact(np.concatenate([[a], xsel]))[None, :]
+            q, sc = orc.quant_act(fmt, row)
+            scale = Fraction(float(sc.reshape(-1)[0]))
+            assert scale == _f32_nearest(Fraction(float(a)) / Fraction(float(qmax))), (fmt, a)
+            for j, x in enumerate(xsel):
+                quot = _f32_nearest(Fraction(float(x)) / scale)
+                if fmt == wl.W8A8_INT8:
+                    n, rem = divmod(quot, 1)
+                    n = int(n) + (1 if rem * 2 > 1 or (rem * 2 == 1 and int(n) % 2 == 1) else 0)
+                    want = min(n, 127)
+                else:
+                    want = int(orc.e4m3_encode(np.array([float(quot)], dtype=np.float32))[0])
+                got = int(q[0, j + 1]) if fmt != wl.W8A8_INT8 else int(q[0, j + 1].astype(np.int8))
+                assert got == want, (fmt, float(a), float(x), got, want)
+                checked[fmt] += 1
+    assert min(checked.values()) >= 20, checked
