@@ -67,7 +67,7 @@ def test_full_size_layers(fmt, layer):
     del w
     assert np.array_equal(as_u8(wq), qw), "weight codes differ"
     assert np.array_equal(ws.cpu().numpy().view(np.uint32), sw.view(np.uint32))
-    for M in (1, 7, 32):
+    for M in (1, 2, 4, 7, 16, 24, 32):   # one token count in each tuned bucket
         x = wl.activations(fmt, N, K, M)
         qa, sa = oracle.quant_act(fmt, x)
         xq, xs, y = gpu_linear(fmt, x, wq, ws, N, None)       # the table's schedule
