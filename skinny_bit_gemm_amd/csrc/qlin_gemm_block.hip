@@ -13,7 +13,7 @@ static gemm_fn pick(int tile_m, int nr, int xc) {
         return tile_m == 64 ? gemm_big_kernel<FMT_BLOCK, 64> : gemm_big_kernel<FMT_BLOCK, 128>;
     }
 #define QLIN_PICK(MT_, NR_, XC_) \
-    if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_) return gemm_kernel<FMT_BLOCK, SWAP, MT_, NR_, QLIN_PF(NR_, XC_), XC_>;
+    if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_) return gemm_kernel<FMT_BLOCK, SWAP, MT_, NR_, QLIN_PF_BLOCK(NR_, XC_), XC_>;
     QLIN_PICK(1, 1, 0) QLIN_PICK(1, 2, 0) QLIN_PICK(1, 4, 0)
     QLIN_PICK(2, 1, 0) QLIN_PICK(2, 2, 0) QLIN_PICK(2, 4, 0)
     QLIN_PICK(1, 1, 2) QLIN_PICK(1, 2, 2) QLIN_PICK(1, 4, 2)
