@@ -903,10 +903,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
 
 // prefetch depth: 8 blocks of 16 weight rows in flight per wave (2 for NR = 4)
 #define QLIN_PF(NR_, XC_) (NR_ >= 4 ? 2 : 8 / NR_)
-// the block format's variants: 6 (3 for NR = 2), ~1 % faster on its
-// workload (each of its slots also waits for a block scale, and every block
-// is scaled on the vector ALU); the other formats measured 3 % slower so
-#define QLIN_PF_BLOCK(NR_, XC_) (NR_ >= 4 ? 2 : 6 / NR_)
+// the block format's variants: 4 blocks (2 for NR = 2, 1 for NR = 4).  Each
+// of its slots also waits for a block scale, and every block is scaled on
+// the vector ALU; on its workload 4 measured ~3 % faster than 8, 6 in
+// between, 2 slower.  The other formats measured 3 % slower at 6.
+#define QLIN_PF_BLOCK(NR_, XC_) (NR_ >= 4 ? 1 : 4 / NR_)
 
 typedef void (*gemm_fn)(GemmLaunch);
 
