@@ -1,5 +1,11 @@
 """Helpers for the GPU parity tests: move numpy inputs to the device, run the
-HIP path through the C ABI binding, bring results back as numpy."""
+HIP path through the C ABI binding, bring results back as numpy.
+
+Every buffer the library writes (outputs, codes, scales, split-K workspaces)
+is allocated by `guarded`: a view into a larger device buffer with 4 KiB
+canary bands on both sides.  `check_guards` asserts the bands still hold the
+canary byte, so a write past either end of a buffer fails the test, not only
+a missed write (which the sentinel fills catch)."""
 from __future__ import annotations
 
 import numpy as np
@@ -8,6 +14,48 @@ import torch
 import skinny_bit_gemm_amd as q
 
 DEV = "cuda:0"
+GUARD_BYTES = 4096
+CANARY = 0xA7
+
+
+def guarded(shape, dtype, fill=None) -> torch.Tensor:
+    """A device tensor of `shape` / `dtype` placed between two GUARD_BYTES
+    bands of CANARY bytes (the start stays 16-byte aligned: the caching
+    allocator aligns the base, and the band is a multiple of 16).  `fill`
+    initialises the tensor itself (default: left at the canary bytes)."""
+    shape = tuple(int(s) for s in (shape if isinstance(shape, (tuple, list)) else (shape,)))
+    esize = torch.empty((), dtype=dtype).element_size()
+    nbytes = int(np.prod(shape, dtype=np.int64)) * esize
+    base = torch.full((2 * GUARD_BYTES + nbytes,), CANARY, dtype=torch.uint8, device=DEV)
+    t = base[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(shape)
+    if fill is not None:
+        t.fill_(fill)
+    t._qlin_guard = (base, nbytes)
+    return t
+
+
+def check_guards(*tensors, what: str = ""):
+    """Assert that the canary bands around every guarded tensor are intact
+    (tensors without bands are skipped)."""
+    for t in tensors:
+        g = getattr(t, "_qlin_guard", None)
+        if g is None:
+            continue
+        base, nbytes = g
+        lo = base[:GUARD_BYTES]
+        hi = base[GUARD_BYTES + nbytes:]
+        bad_lo = int((lo != CANARY).sum())
+        bad_hi = int((hi != CANARY).sum())
+        assert bad_lo == 0 and bad_hi == 0, (
+            f"{what}: write outside a {tuple(t.shape)} {t.dtype} buffer "
+            f"({bad_lo} bytes changed before it, {bad_hi} after it)")
+
+
+def check_workspace(work: torch.Tensor, what: str = ""):
+    """The split-K workspace is left zero by every call, and nothing is
+    written around it."""
+    check_guards(work, what=what)
+    assert int(work.count_nonzero()) == 0, f"{what}: workspace not left zero"
 
 
 def to_dev_bf16(x_bits: np.ndarray) -> torch.Tensor:
@@ -31,37 +79,46 @@ def gpu_quant_act(fmt: int, x_bits: np.ndarray, ldx: int | None = None):
         xd = to_dev_bf16(padded)
     else:
         xd = to_dev_bf16(x_bits)
-    xq = torch.empty((M, K), dtype=torch.uint8, device=DEV)
-    xs = torch.empty(q.scales_shape(fmt, M, K, False), dtype=torch.float32, device=DEV)
+    xq = guarded((M, K), torch.uint8, 0x55)
+    xs = guarded(q.scales_shape(fmt, M, K, False), torch.float32, -1.0)
     q.qlin_quantize_act(fmt, M, K, xd, ldx, xq, xs)
     torch.cuda.synchronize()
+    check_guards(xq, xs, what=f"qlin_quantize_act fmt={fmt} M={M} K={K}")
     return xq, xs
 
 
 def gpu_quant_weight(fmt: int, w: np.ndarray):
     N, K = w.shape
     wd = to_dev(w.astype(np.float32))
-    wq = torch.empty((N, K), dtype=torch.uint8, device=DEV)
-    ws = torch.empty(q.scales_shape(fmt, N, K, True), dtype=torch.float32, device=DEV)
+    wq = guarded((N, K), torch.uint8, 0x55)
+    ws = guarded(q.scales_shape(fmt, N, K, True), torch.float32, -1.0)
     q.qlin_quantize_weight(fmt, N, K, wd, wq, ws)
     torch.cuda.synchronize()
+    check_guards(wq, ws, what=f"qlin_quantize_weight fmt={fmt} N={N} K={K}")
     del wd
     return wq, ws
 
 
 def workspace_for(fmt, M, N, K, cfg):
+    """A zeroed split-K workspace of the size the schedule needs, guarded."""
     nbytes = q.qlin_workspace_bytes(fmt, M, N, K, cfg)
-    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    return guarded((max(nbytes, 16),), torch.uint8, 0)
+
+
+def out_dtype(out_type):
+    return {q.QLIN_OUT_BF16: torch.int16, q.QLIN_OUT_F32_ACC: torch.float32,
+            q.QLIN_OUT_I32_ACC: torch.int32}[out_type]
 
 
 def gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, cfg=None, out_type=q.QLIN_OUT_BF16, workspace=None):
-    dt = {q.QLIN_OUT_BF16: torch.int16, q.QLIN_OUT_F32_ACC: torch.float32,
-          q.QLIN_OUT_I32_ACC: torch.int32}[out_type]
-    y = torch.full((M, N), -1, dtype=dt, device=DEV)   # sentinel: every element must be written
+    y = guarded((M, N), out_dtype(out_type), -1)   # sentinel: every element must be written
     if workspace is None:
         workspace = workspace_for(fmt, M, N, K, cfg)
     q.qlin_gemm(fmt, M, N, K, xq, xs, wq, ws, y, out_type, cfg, workspace)
     torch.cuda.synchronize()
+    what = f"qlin_gemm fmt={fmt} M={M} N={N} K={K} cfg={cfg}"
+    check_guards(y, what=what)
+    check_workspace(workspace, what=what)
     return y
 
 
@@ -83,13 +140,14 @@ def gpu_linear(fmt, x_bits, wq, ws, N, cfg=None, out_type=q.QLIN_OUT_BF16, works
     padded = np.zeros((M, ldx), dtype=np.uint16)
     padded[:, :K] = x_bits
     xd = to_dev_bf16(padded)
-    xq = torch.full((M, K), 0x55, dtype=torch.uint8, device=DEV)
-    xs = torch.full(q.scales_shape(fmt, M, K, False), -1.0, dtype=torch.float32, device=DEV)
-    dt = {q.QLIN_OUT_BF16: torch.int16, q.QLIN_OUT_F32_ACC: torch.float32,
-          q.QLIN_OUT_I32_ACC: torch.int32}[out_type]
-    y = torch.full((M, N), -1, dtype=dt, device=DEV)
+    xq = guarded((M, K), torch.uint8, 0x55)
+    xs = guarded(q.scales_shape(fmt, M, K, False), torch.float32, -1.0)
+    y = guarded((M, N), out_dtype(out_type), -1)
     if workspace is None:
         workspace = workspace_for(fmt, M, N, K, cfg)
     q.qlin_linear(fmt, M, N, K, xd, ldx, xq, xs, wq, ws, y, out_type, cfg, workspace)
     torch.cuda.synchronize()
+    what = f"qlin_linear fmt={fmt} M={M} N={N} K={K} cfg={cfg}"
+    check_guards(xq, xs, y, what=what)
+    check_workspace(workspace, what=what)
     return xq, xs, y

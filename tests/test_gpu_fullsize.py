@@ -2,10 +2,14 @@
 benchmark times (qlin_linear with the selection table's schedule), and the
 crossover sweep above 32 tokens with every schedule forced.
 
-Codes and scales are compared in full; outputs on a sample of positions the
-oracle computes one by one (corners, tile edges and random positions).  The
-tolerance's max|ref| is taken over the sampled references, which is never
-larger than over the whole output, so the bound is if anything stricter."""
+The layers of the three model workloads are compared in full at every token
+count: codes, scales, the whole bf16 output against oracle.gemm (and, for
+W8A8_INT8, the whole int32 accumulator array bit for bit).  The crossover
+sweep compares whole outputs at 64 tokens and a sample of positions the
+oracle computes one by one (corners, tile edges and random positions) above;
+there the tolerance's max|ref| is taken over the sampled references, which
+is never larger than over the whole output, so the bound is if anything
+stricter.  Every output buffer sits between canary bands (tests/_gpu.py)."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +20,7 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import DEV, as_u8, gpu_gemm, gpu_linear, gpu_quant_weight, to_dev  # noqa: E402
+from _gpu import DEV, as_u8, gpu_gemm, gpu_linear, gpu_quant_weight, to_dev, y_to_numpy  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -56,6 +60,25 @@ BENCH_SHAPES = [(wl.FP8_DYNAMIC, L) for L in wl.SMALL_DENSE] + \
     [(wl.W8A8_INT8, L) for L in wl.DENSE_8B] + [(wl.BLOCK_FP8, L) for L in wl.DENSE_32B]
 
 
+def oracle_whole(fmt, qa, sa, qw, sw):
+    """(ref, int32 accumulators or None) of the whole product."""
+    if fmt == wl.W8A8_INT8:
+        return oracle.gemm(fmt, qa, sa, qw, sw, want_acc=True)
+    return oracle.gemm(fmt, qa, sa, qw, sw), None
+
+
+def check_whole(fmt, y, qa, sa, qw, sw, acc_y=None, what="", expected=None):
+    """The whole output against oracle.gemm (tolerance with max|ref| over
+    the call's whole output), and the int32 accumulators bit for bit.
+    `expected` = oracle_whole(...) when already computed."""
+    ref, acc = expected if expected is not None else oracle_whole(fmt, qa, sa, qw, sw)
+    if acc_y is not None:
+        bad = int(np.count_nonzero(acc_y != acc))
+        assert bad == 0, f"{what}: {bad} int32 accumulators differ"
+    ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
+    assert ok, f"{what}: outputs outside tolerance (worst ratio {worst:.3g})"
+
+
 @pytest.mark.parametrize("fmt,layer", BENCH_SHAPES,
                          ids=[f"{wl.FORMAT_NAMES[f]}-{L.name}" for f, L in BENCH_SHAPES])
 def test_full_size_layers(fmt, layer):
@@ -70,6 +93,7 @@ def test_full_size_layers(fmt, layer):
     for M in (1, 2, 4, 7, 16, 24, 32):   # one token count in each tuned bucket
         x = wl.activations(fmt, N, K, M)
         qa, sa = oracle.quant_act(fmt, x)
+        print(f"[full]   M={M} schedule={q.qlin_select_variant(fmt, M, N, K)}", flush=True)
         xq, xs, y = gpu_linear(fmt, x, wq, ws, N, None)       # the table's schedule
         assert np.array_equal(as_u8(xq), qa), f"M={M}: activation codes differ"
         assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa.view(np.uint32))
@@ -77,7 +101,7 @@ def test_full_size_layers(fmt, layer):
         if fmt == wl.W8A8_INT8:
             _, _, yi = gpu_linear(fmt, x, wq, ws, N, None, out_type=q.QLIN_OUT_I32_ACC)
             acc_y = yi.cpu().numpy()
-        check_sampled(fmt, y, qa, sa, qw, sw, M, N, acc_y, seed=M)
+        check_whole(fmt, y, qa, sa, qw, sw, acc_y, what=f"M={M}")
 
 
 def forced(fmt, M, N, K):
@@ -100,7 +124,8 @@ def forced(fmt, M, N, K):
 @pytest.mark.parametrize("layer", wl.DENSE_8B, ids=[L.name for L in wl.DENSE_8B])
 def test_crossover_sweep_variants(fmt, layer):
     """All three formats on the 8B-class shapes at M = 64 .. 512, every
-    schedule forced, against the oracle (sampled outputs)."""
+    schedule forced, against the oracle (whole outputs at 64 tokens, sampled
+    outputs above)."""
     N, K = layer.N, layer.K
     print(f"[sweep] fmt={fmt} {layer.name} N={N} K={K}", flush=True)
     w = wl.weights(fmt, N, K)
@@ -112,10 +137,15 @@ def test_crossover_sweep_variants(fmt, layer):
         qa, sa = oracle.quant_act(fmt, x)
         xq = to_dev(qa)
         xs = to_dev(sa)
+        expected = oracle_whole(fmt, qa, sa, qw, sw) if M == 64 else None
         for name, c in forced(fmt, M, N, K).items():
+            print(f"[sweep]   M={M} {name} cfg={c}", flush=True)
             y = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c)
             acc_y = None
             if fmt == wl.W8A8_INT8:
                 acc_y = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, q.QLIN_OUT_I32_ACC).cpu().numpy()
-            check_sampled(fmt, y, qa, sa, qw, sw, M, N, acc_y, seed=M + len(name))
+            if M == 64:
+                check_whole(fmt, y, qa, sa, qw, sw, acc_y, what=f"M={M} {name}", expected=expected)
+            else:
+                check_sampled(fmt, y, qa, sa, qw, sw, M, N, acc_y, seed=M + len(name))
         del xq, xs

@@ -11,7 +11,8 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import DEV, as_u8, gpu_quant_weight, to_dev_bf16, workspace_for  # noqa: E402
+from _gpu import (DEV, as_u8, check_guards, check_workspace, gpu_quant_weight, guarded,  # noqa: E402
+                  to_dev_bf16, workspace_for)
 
 FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
 FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
@@ -31,11 +32,17 @@ class Layer:
         self.w_np = wl.random_weights(N, K, seed)
         self.x = to_dev_bf16(self.x_np)
         self.wq, self.ws = gpu_quant_weight(fmt, self.w_np)
-        self.xq = torch.empty((M, K), dtype=torch.uint8, device=DEV)
-        self.xs = torch.empty(q.scales_shape(fmt, M, K, False), dtype=torch.float32, device=DEV)
-        self.y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+        self.xq = guarded((M, K), torch.uint8)
+        self.xs = guarded(q.scales_shape(fmt, M, K, False), torch.float32)
+        self.y = guarded((M, N), torch.int16)
         self.cfg = cfg
         self.work = workspace_for(fmt, M, N, K, cfg)
+
+    def check_guards(self, what):
+        """Nothing written around the layer's outputs and workspace, and the
+        workspace left zero."""
+        check_guards(self.xq, self.xs, self.y, what=what)
+        check_workspace(self.work, what=what)
 
     def run(self, stream):
         q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, self.wq,
@@ -64,6 +71,8 @@ def test_graph_replays_equal_eager(fmt):
         for l in layers:
             l.run(stream)
         torch.cuda.synchronize()
+        for l in layers:
+            l.check_guards("eager")
         eager = [(l.xq.clone(), l.xs.clone(), l.y.clone()) for l in layers]
         g = capture(stream, layers)
         for rep in range(6):
@@ -78,6 +87,7 @@ def test_graph_replays_equal_eager(fmt):
                 assert torch.equal(l.xs, xs), f"replay {rep}: scales differ"
                 # every reduction is order-independent, so replays are bit-identical
                 assert torch.equal(l.y, y), f"replay {rep}: outputs differ"
+                l.check_guards(f"replay {rep}")
             # eager work of the program between replays
             for l in layers[:2]:
                 l.run(stream)
@@ -104,7 +114,7 @@ def test_graph_int8_bit_identical_over_100_replays():
             q.qlin_graph_launch(g, stream)
         torch.cuda.synchronize()
         assert torch.equal(l.y, first)
-        assert int(l.work.count_nonzero()) == 0
+        l.check_guards("after 100 replays")
         q.qlin_graph_destroy(g)
 
 

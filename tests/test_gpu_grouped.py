@@ -16,7 +16,8 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import DEV, as_u8, gpu_quant_act, to_dev, y_to_numpy  # noqa: E402
+from _gpu import (DEV, as_u8, check_guards, check_workspace, gpu_quant_act, guarded, out_dtype,  # noqa: E402
+                  to_dev, y_to_numpy)
 
 FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
 FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
@@ -60,14 +61,15 @@ def experts(fmt, E, N, K, seed):
 
 def run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, max_rows, c, out_type=q.QLIN_OUT_BF16):
     total = int(offsets[-1])
-    dt = {q.QLIN_OUT_BF16: torch.int16, q.QLIN_OUT_I32_ACC: torch.int32}[out_type]
-    y = torch.full((total, N), -1, dtype=dt, device=DEV)    # sentinel: every row must be written
+    y = guarded((total, N), out_dtype(out_type), -1)    # sentinel: every row must be written
     nb = q.qlin_grouped_workspace_bytes(fmt, E, N, K, total, max_rows, c)
-    work = torch.zeros(max(nb, 16), dtype=torch.uint8, device=DEV)
+    work = guarded((max(nb, 16),), torch.uint8, 0)
     off = to_dev(offsets.astype(np.int32))
     q.qlin_grouped_gemm(fmt, E, N, K, off, total, max_rows, xq, xs, wqd, wsd, y, out_type, c, work)
     torch.cuda.synchronize()
-    assert not torch.any(work != 0), "workspace not left zero"
+    what = f"qlin_grouped_gemm fmt={fmt} E={E} N={N} K={K} rows={total} cfg={c}"
+    check_guards(y, what=what)
+    check_workspace(work, what=what)
     return y
 
 
@@ -136,7 +138,7 @@ def test_grouped_graph_replays_follow_new_routing():
     xq = torch.empty((total, K), dtype=torch.uint8, device=DEV)
     xs = torch.empty((total,), dtype=torch.float32, device=DEV)
     off = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
-    y = torch.empty((total, N), dtype=torch.int32, device=DEV)
+    y = guarded((total, N), torch.int32)
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
         q.qlin_graph_begin(st)
@@ -156,6 +158,7 @@ def test_grouped_graph_replays_follow_new_routing():
             st.synchronize()
             _, acc = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw, want_acc=True)
             assert np.array_equal(y.cpu().numpy(), acc), f"replay {seed}"
+            check_guards(y, what=f"grouped graph replay {seed}")
     finally:
         q.qlin_graph_destroy(g)
 
@@ -190,10 +193,11 @@ def test_grouped_moe_layer_shape(fmt, layer, T):
 
 def test_grouped_no_rows_is_a_no_op():
     E, N, K = 4, 256, 512
-    y = torch.full((1, N), -1, dtype=torch.int16, device=DEV)
+    y = guarded((1, N), torch.int16, -1)
     off = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
     z = torch.zeros((E, N, K), dtype=torch.uint8, device=DEV)
     s = torch.zeros((E, N), dtype=torch.float32, device=DEV)
     q.qlin_grouped_gemm(wl.FP8_DYNAMIC, E, N, K, off, 0, 4, z, s, z, s, y)
     torch.cuda.synchronize()
     assert torch.all(y == -1)
+    check_guards(y, what="grouped, no rows")

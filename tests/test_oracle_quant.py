@@ -225,23 +225,12 @@ def test_codes_come_from_the_ieee_quotient(orc):
     from a search over bf16 values for those where the two quotients give
     different codes; both formats must meet at least 20 of them."""
     from fractions import Fraction
-    bf = (np.arange(0x0080, 0x7F80, dtype=np.uint32) << 16).view(np.float32)   # positive normal bf16
-    rng = np.random.default_rng(1)
-    amaxes = rng.choice(bf[(bf > 1e-3) & (bf < 1e3)], 300, replace=False)
+    from _quotient_pairs import quotient_pairs
     checked = {wl.W8A8_INT8: 0, wl.FP8_DYNAMIC: 0}
     for fmt in checked:
         qmax = np.float32(QMAX[fmt])
-        for a in amaxes:
-            s = np.float32(a) / qmax
-            xs = bf[bf <= a]
-            qd, qr = xs / s, xs * (np.float32(1.0) / s)
-            if fmt == wl.W8A8_INT8:
-                sel = np.rint(qd) != np.rint(qr)
-            else:
-                sel = orc.e4m3_encode(qd) != orc.e4m3_encode(qr)
-            if not sel.any():
-                continue
-            xsel = xs[sel][:8]
+        encode = None if fmt == wl.W8A8_INT8 else orc.e4m3_encode
+        for a, xsel in quotient_pairs(qmax, encode, n_amax=300, per_amax=8, seed=1):
             row = _f32_to_bf16_exact(np.concatenate([[a], xsel]))[None, :]
             q, sc = orc.quant_act(fmt, row)
             scale = Fraction(float(sc.reshape(-1)[0]))
