@@ -26,7 +26,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "skinny W8A8 GEMM achieved HBM GB/s & TFLOP/s at M=1..32, % of roofline"
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "fp8_dynamic_hidden2048"
+# the headline: the largest of the three model workloads (BlockFP8 on the
+# hidden-5120 layer shapes); the other two are timed beside it (--also)
+DEFAULT_WORKLOAD = "block_fp8_hidden5120"
+DEFAULT_ALSO = "fp8_dynamic_hidden2048,w8a8_int8_hidden4096"
 DTYPE = {0: "fp8_e4m3", 1: "int8", 2: "fp8_e4m3"}
 
 
@@ -36,6 +39,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default=DEFAULT_ALSO,
+                    help="other workloads whose step and GEMM launches are timed the same way and "
+                         "reported under other_workloads ('' for none)")
+    ap.add_argument("--floors", default=None,
+                    help="instead of the step: time the graph-replayed streaming read of every layer "
+                         "size of the three model workloads and write it (JSON) here")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -431,40 +440,20 @@ def moe_bench(path, fmts, Ts, layers=None, schedules=None):
             "geomean_rule_GBps": geomean("rule"), "geomean_per_expert_GBps": geomean("per_expert_launches")}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+def run_workload(name, steps, warmup, detail=False, gemm_only_steps=None, floors=None):
+    """Times one workload's step: every (M, layer) linear of it, replayed
+    from hipGraphs over rotating weight copies; then the step's GEMM kernels
+    alone (the roofline entry).  With `detail`, also every linear alone
+    (`floors`: graph-replayed streaming-read times per weight size, for the
+    kernel / floor column).  Returns the numbers as a dict."""
     import torch
 
     import skinny_bit_gemm_amd as q
     from skinny_bit_gemm_amd.tune import warm_graph
     import workloads as wl
 
-    if args.workload not in wl.WORKLOADS:
-        sys.exit(f"unknown workload {args.workload}; choose from {sorted(wl.WORKLOADS)}")
-    if args.moe:
-        fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
-        Ts = [int(t) for t in args.moe_tokens.split(",")] if args.moe_tokens else list(wl.MOE_TOKENS)
-        if args.calibrate_copy:
-            calibrate_copy(args.calibrate_copy)
-        print(json.dumps(moe_bench(args.moe, fmts, Ts, args.moe_layers and args.moe_layers.split(","),
-                                   args.moe_schedules and args.moe_schedules.split(","))), flush=True)
-        return
-    if args.sweep:
-        fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
-        print(json.dumps(crossover_sweep(args.sweep, fmts, [int(m) for m in args.sweep_m.split(",")])),
-              flush=True)
-        return
-    fmt, layers, Ms = wl.WORKLOADS[args.workload]
+    fmt, layers, Ms = wl.WORKLOADS[name]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    q.lib()
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-
     # quantized weights (GPU quantizer, offline and untimed), then rotating copies
     base = {}
     for L in layers:
@@ -506,29 +495,30 @@ def main():
         step_flops = sum(l.flops for l in sets[0])
         n_gemm = len(sets[0])
 
-        if args.gemm_only_steps:
-            for i in range(args.gemm_only_steps):
+        if gemm_only_steps:
+            for i in range(gemm_only_steps):
                 q.qlin_graph_launch(gemm_graphs[i % n_sets], stream)
             torch.cuda.synchronize()
-            print(json.dumps({"gemm_only_steps": args.gemm_only_steps, "launches": n_gemm * args.gemm_only_steps}))
-            return
+            for g in step_graphs + gemm_graphs:
+                q.qlin_graph_destroy(g)
+            return {"gemm_only_steps": gemm_only_steps, "launches": n_gemm * gemm_only_steps}
 
         # set-up (weight preparation, the eager pass, capture) leaves the GPU
         # idle; replaying the step for ~20 ms, untimed, before the warm-up
         # steps brings it back to its steady rate whatever --warmup is
         for g in step_graphs:
             warm_graph(g, stream, min_ms=20.0 / n_sets)
-        for i in range(args.warmup):
+        for i in range(warmup):
             q.qlin_graph_launch(step_graphs[i % n_sets], stream)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(steps):
             q.qlin_graph_launch(step_graphs[i % n_sets], stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        ms_step = e0.elapsed_time(e1) / args.steps
+        ms_step = e0.elapsed_time(e1) / steps
 
         # the step's GEMM kernels alone (same launches, same order; the fused
         # ones include their quantization), for the roofline
@@ -537,14 +527,14 @@ def main():
         for i in range(2):
             q.qlin_graph_launch(gemm_graphs[i % n_sets], stream)
         g0.record(stream)
-        for i in range(args.steps):
+        for i in range(steps):
             q.qlin_graph_launch(gemm_graphs[i % n_sets], stream)
         g1.record(stream)
         torch.cuda.synchronize()
-        ms_gemms = g0.elapsed_time(g1) / args.steps
+        ms_gemms = g0.elapsed_time(g1) / steps
 
-        detail = []
-        if args.detail:
+        rows = []
+        if detail:
             # per (M, layer): graphs of the whole linear and of its GEMM
             # kernel over >= 1 GiB of copies of that layer's weights (fewer
             # would leave a small layer's copies in the L2 and Infinity Cache)
@@ -570,20 +560,122 @@ def main():
                 layer_us = per_launch_us(copies, lambda w: l0.layer(stream, w))
                 kernel_us = per_launch_us(copies, lambda w: l0.kernel(stream, w))
                 del copies
-                detail.append({"layer": l0.name, "M": l0.M, "N": l0.N, "K": l0.K, "fused": l0.fused,
-                               "layer_us": round(layer_us, 3),
-                               "layer_GBps": round((l0.bytes + l0.qbytes) / layer_us / 1e3, 1),
-                               "layer_TFLOPs": round(l0.flops / layer_us / 1e6, 3),
-                               "kernel_us": round(kernel_us, 3),
-                               "kernel_GBps": round(l0.kernel_bytes / kernel_us / 1e3, 1),
-                               "kernel_frac_hbm": round(l0.kernel_bytes / kernel_us / 1e3 / HBM_PEAK_GBS, 4),
-                               "cfg": l0.cfg.as_dict()})
+                rows.append({"layer": l0.name, "M": l0.M, "N": l0.N, "K": l0.K, "fused": l0.fused,
+                             "layer_us": round(layer_us, 3),
+                             "layer_GBps": round((l0.bytes + l0.qbytes) / layer_us / 1e3, 1),
+                             "layer_TFLOPs": round(l0.flops / layer_us / 1e6, 3),
+                             "kernel_us": round(kernel_us, 3),
+                             "kernel_GBps": round(l0.kernel_bytes / kernel_us / 1e3, 1),
+                             "kernel_frac_hbm": round(l0.kernel_bytes / kernel_us / 1e3 / HBM_PEAK_GBS, 4),
+                             "cfg": l0.cfg.as_dict()})
 
     for g in step_graphs + gemm_graphs:
         q.qlin_graph_destroy(g)
+    if floors:
+        for d in rows:
+            f = floors.get(d["N"] * d["K"])
+            if f:
+                d["floor_us"] = f
+                d["kernel_over_floor"] = round(d["kernel_us"] / f, 3)
+    res = {"workload": name, "fmt": fmt, "layers": layers, "Ms": Ms, "n_gemm": n_gemm, "n_sets": n_sets,
+           "ms_step": ms_step, "ms_gemms": ms_gemms, "step_bytes": step_bytes, "gemm_bytes": gemm_bytes,
+           "step_flops": step_flops, "detail": rows}
+    del sets, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = gemm_bytes / (ms_gemms * 1e-3) / 1e9
+
+def floors_bench(path):
+    """Graph-replayed streaming-read time of a buffer of each layer's weight
+    size (cold copies, >= 1 GiB in all): the floor a kernel that reads the
+    layer's weights once would meet under the layer timings' conditions."""
+    from skinny_bit_gemm_amd import probe
+    import workloads as wl
+    rows = []
+    seen = set()
+    for name in ("fp8_dynamic_hidden2048", "w8a8_int8_hidden4096", "block_fp8_hidden5120"):
+        _, layers, _ = wl.WORKLOADS[name]
+        for L in layers:
+            nb = L.N * L.K
+            if nb in seen:
+                continue
+            seen.add(nb)
+            us, blocks = probe.graph_floor_us(nb, with_grid=True)
+            rows.append({"workload": name, "layer": L.name, "N": L.N, "K": L.K, "bytes": nb,
+                         "floor_us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "best_grid": blocks})
+            print(f"[floors] {name} {L.name} {nb} B: {us:.3f} us", file=sys.stderr, flush=True)
+    ceiling = probe.read_ceiling_gbs()
+    with open(path, "w") as f:
+        json.dump({"read_ceiling_GBps": round(ceiling, 1), "floors": rows}, f, indent=1)
+    return {"mode": "floors", "sizes": len(rows), "file": path, "read_ceiling_GBps": round(ceiling, 1)}
+
+
+def workload_summary(r):
+    """Step and GEMM-launch numbers of one timed workload."""
+    value = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    achieved = r["gemm_bytes"] / (r["ms_gemms"] * 1e-3) / 1e9
+    return {"step_GBps": round(value, 2), "ms_per_step": round(r["ms_step"], 5),
+            "step_TFLOPs": round(r["step_flops"] / (r["ms_step"] * 1e-3) / 1e12, 3),
+            "gemm_achieved_GBps": round(achieved, 1), "gemm_frac": round(achieved / HBM_PEAK_GBS, 4),
+            "gemm_avg_launch_us": round(r["ms_gemms"] * 1e3 / r["n_gemm"], 3),
+            "linears_per_step": r["n_gemm"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import skinny_bit_gemm_amd as q
+    import workloads as wl
+
+    if args.workload not in wl.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(wl.WORKLOADS)}")
+    also = [w for w in args.also.split(",") if w and w != args.workload] if args.also else []
+    for w in also:
+        if w not in wl.WORKLOADS:
+            sys.exit(f"unknown workload {w} in --also; choose from {sorted(wl.WORKLOADS)}")
+    if args.moe:
+        fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
+        Ts = [int(t) for t in args.moe_tokens.split(",")] if args.moe_tokens else list(wl.MOE_TOKENS)
+        if args.calibrate_copy:
+            calibrate_copy(args.calibrate_copy)
+        print(json.dumps(moe_bench(args.moe, fmts, Ts, args.moe_layers and args.moe_layers.split(","),
+                                   args.moe_schedules and args.moe_schedules.split(","))), flush=True)
+        return
+    if args.sweep:
+        fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
+        print(json.dumps(crossover_sweep(args.sweep, fmts, [int(m) for m in args.sweep_m.split(",")])),
+              flush=True)
+        return
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q.lib()
+    if args.floors:
+        print(json.dumps(floors_bench(args.floors)), flush=True)
+        return
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+    if args.gemm_only_steps:
+        print(json.dumps(run_workload(args.workload, args.steps, args.warmup,
+                                      gemm_only_steps=args.gemm_only_steps)), flush=True)
+        return
+
+    floors = None
+    if args.detail:
+        from skinny_bit_gemm_amd import probe
+        _, layers, _ = wl.WORKLOADS[args.workload]
+        floors = {L.N * L.K: round(probe.graph_floor_us(L.N * L.K), 3) for L in layers}
+    r = run_workload(args.workload, args.steps, args.warmup, detail=bool(args.detail), floors=floors)
+    print(f"[bench] {args.workload}: {json.dumps(workload_summary(r))}", file=sys.stderr, flush=True)
+    fmt, layers, Ms, n_gemm = r["fmt"], r["layers"], r["Ms"], r["n_gemm"]
+    detail = r["detail"]
+    value = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    achieved = r["gemm_bytes"] / (r["ms_gemms"] * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -591,7 +683,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(r["ms_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -603,10 +695,10 @@ def main():
             "layers": {L.name: [L.N, L.K] for L in layers},
             "token_counts": list(Ms),
             "linears_per_step": n_gemm,
-            "weight_copies": n_sets,
+            "weight_copies": r["n_sets"],
             "graph_replay": True,
         },
-        "tflops": round(step_flops / (ms_step * 1e-3) / 1e12, 3),
+        "tflops": round(r["step_flops"] / (r["ms_step"] * 1e-3) / 1e12, 3),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -615,8 +707,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
             "kernel": "gemm_kernel (every launch of a step; the fused ones include their quantization)",
-            "avg_launch_us": round(ms_gemms * 1e3 / n_gemm, 3),
-            "bytes_per_launch": round(gemm_bytes / n_gemm),
+            "avg_launch_us": round(r["ms_gemms"] * 1e3 / n_gemm, 3),
+            "bytes_per_launch": round(r["gemm_bytes"] / n_gemm),
         },
     }
     if not args.no_read_ceiling:
@@ -644,9 +736,23 @@ def main():
         }
         with open(args.detail, "w") as f:
             json.dump({"summary": summary, "shapes": detail}, f, indent=1)
+    if also:
+        # the other workloads, step and GEMM launches timed the same way
+        # (each with its own traffic record when it matches the sources)
+        out["other_workloads"] = {}
+        for w in also:
+            ro = run_workload(w, args.steps, args.warmup)
+            summ = workload_summary(ro)
+            tro = measured_traffic(w)
+            summ["traffic_vs_algorithmic"] = (round(tro["per_launch_traffic_bytes"] /
+                                                    tro["per_launch_algorithmic_bytes"], 3) if tro else None)
+            print(f"[bench] {w}: {json.dumps(summ)}", file=sys.stderr, flush=True)
+            out["other_workloads"][w] = summ
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(fmt, layers, Ms, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
 
 
 if __name__ == "__main__":

@@ -55,3 +55,18 @@ def test_moe_schedules_are_valid_grouped_configs():
                 for name, c in bench.moe_configs(q, fmt, T).items():
                     # every forced schedule plans for the layer (no launch)
                     assert q.qlin_grouped_workspace_bytes(fmt, E, L.N, L.K, T * wl.MOE_TOPK, T, c) >= 0, name
+
+
+def test_headline_is_the_largest_workload_and_the_others_ride_along():
+    """The default run times BlockFP8 on the hidden-5120 shapes (the largest
+    of the three model workloads) and reports the other two beside it."""
+    assert bench.DEFAULT_WORKLOAD == "block_fp8_hidden5120"
+    fmt, layers, Ms = wl.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    sizes = {w: sum(L.N * L.K for L in wl.WORKLOADS[w][1]) for w in
+             ("fp8_dynamic_hidden2048", "w8a8_int8_hidden4096", "block_fp8_hidden5120")}
+    assert max(sizes, key=sizes.get) == bench.DEFAULT_WORKLOAD
+    also = bench.DEFAULT_ALSO.split(",")
+    assert sorted(also + [bench.DEFAULT_WORKLOAD]) == sorted(sizes)
+    r = {"step_bytes": 2e9, "ms_step": 1.0, "step_flops": 1e12, "gemm_bytes": 4e9, "ms_gemms": 1.0, "n_gemm": 28}
+    s = bench.workload_summary(r)
+    assert s["step_GBps"] == 2000.0 and s["gemm_achieved_GBps"] == 4000.0 and s["gemm_frac"] == 0.5
