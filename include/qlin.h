@@ -165,6 +165,32 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
                         qlin_out_type out_type, const qlin_config *cfg, void *workspace,
                         size_t ws_bytes, void *stream);
 
+/* Bytes of the static split-K workspace that qlin_linear_scratch uses on
+ * each GPU. */
+#define QLIN_SCRATCH_BYTES (8u << 20)
+
+/* qlin_linear for callers that cannot allocate device memory: code under
+ * hipGraph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, layouts, results and errors are qlin_linear's, minus the
+ * workspace: a schedule that splits K keeps its partial sums and arrival
+ * counters in a static array of QLIN_SCRATCH_BYTES that the library holds
+ * on each GPU until the process ends.  Nothing is allocated or freed.
+ *   - a schedule whose workspace (qlin_workspace_bytes) exceeds
+ *     QLIN_SCRATCH_BYTES is rejected with QLIN_ERR_WORKSPACE before any
+ *     HIP call (every M <= 32 entry of the shipped table fits);
+ *   - the array must hold zeros between calls, and every call leaves it so;
+ *     the first call on a GPU that needs it enqueues one fill kernel on
+ *     `stream` that zeroes it (a call made while `stream` is captured puts
+ *     the fill into the graph, and the next call outside capture fills it
+ *     once more);
+ *   - every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other threads, or a graph replay
+ *     beside an eager call) race on it and their results are undefined. */
+qlin_status qlin_linear_scratch(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx,
+                                void *xq, float *x_scales, const void *wq, const float *w_scales,
+                                void *y, qlin_out_type out_type, const qlin_config *cfg,
+                                void *stream);
+
 /* Schedule lookup (host only, no device work).  M rounds up to the next
  * tuned token bucket {1,2,4,8,16,24,32} (section "Per-shape Config Tuning"),
  * or {64,128,256,512} above 32.  In strict mode a missing entry is

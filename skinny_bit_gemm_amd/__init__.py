@@ -32,7 +32,10 @@ EXPORTS = (
     "qlin_table_entries", "qlin_graph_begin", "qlin_graph_end", "qlin_graph_launch",
     "qlin_graph_destroy", "qlin_status_str", "qlin_abi_version", "qlin_last_hip_error",
     "qlin_grouped_gemm", "qlin_grouped_select_variant", "qlin_grouped_workspace_bytes",
+    "qlin_linear_scratch",
 )
+# bytes of the static split-K workspace of qlin_linear_scratch (per GPU)
+QLIN_SCRATCH_BYTES = 8 << 20
 
 
 class QlinError(RuntimeError):
@@ -89,6 +92,8 @@ def lib():
                                 ctypes.POINTER(qlin_config), _P, _SZ, _P]
         L.qlin_linear.argtypes = [_I, _I, _I, _I, _P, _I64, _P, _P, _P, _P, _P, _I,
                                   ctypes.POINTER(qlin_config), _P, _SZ, _P]
+        L.qlin_linear_scratch.argtypes = [_I, _I, _I, _I, _P, _I64, _P, _P, _P, _P, _P, _I,
+                                          ctypes.POINTER(qlin_config), _P]
         L.qlin_select_variant.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config)]
         L.qlin_workspace_bytes.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config),
                                            ctypes.POINTER(_SZ)]
@@ -170,6 +175,14 @@ def qlin_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type=QL
                            _ptr(w_scales), _ptr(y), out_type, cptr, _ptr(workspace), ws_bytes,
                            _stream(stream))
     return _check(st, "qlin_linear", raise_on_error)
+
+
+def qlin_linear_scratch(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type=QLIN_OUT_BF16,
+                        cfg=None, stream=None, raise_on_error=True):
+    cptr = ctypes.byref(cfg) if cfg is not None else None
+    st = lib().qlin_linear_scratch(fmt, M, N, K, _ptr(x), ldx, _ptr(xq), _ptr(x_scales), _ptr(wq),
+                                   _ptr(w_scales), _ptr(y), out_type, cptr, _stream(stream))
+    return _check(st, "qlin_linear_scratch", raise_on_error)
 
 
 def qlin_select_variant(fmt, M, N, K) -> qlin_config:

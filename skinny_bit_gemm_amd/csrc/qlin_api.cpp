@@ -236,11 +236,11 @@ qlin_status qlin_workspace_bytes(qlin_format fmt, int M, int N, int K, const qli
 }
 
 // Checks shared by qlin_gemm and qlin_linear (everything but the
-// activations); fills *c and *p.
-static qlin_status check_gemm(qlin_format fmt, int M, int N, int K, const float *x_scales,
-                              const void *wq, const float *w_scales, void *y,
-                              qlin_out_type out_type, const qlin_config *cfg, void *workspace,
-                              size_t ws_bytes, bool fused, qlin_config *c, Plan *p) {
+// activations and the workspace); fills *c and *p.
+static qlin_status check_gemm_args(qlin_format fmt, int M, int N, int K, const float *x_scales,
+                                   const void *wq, const float *w_scales, void *y,
+                                   qlin_out_type out_type, const qlin_config *cfg, bool fused,
+                                   qlin_config *c, Plan *p) {
     if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
     if (out_type != QLIN_OUT_BF16 && out_type != QLIN_OUT_F32_ACC && out_type != QLIN_OUT_I32_ACC)
         return QLIN_ERR_INVALID_ARG;
@@ -252,13 +252,24 @@ static qlin_status check_gemm(qlin_format fmt, int M, int N, int K, const float 
         return QLIN_ERR_ALIGNMENT;
     st = resolve_config(fmt, M, N, K, cfg, c);
     if (st != QLIN_OK) return st;
-    st = make_plan(fmt, M, N, K, *c, fused, p);
-    if (st != QLIN_OK) return st;
-    if (p->ws_bytes > 0) {
-        if (!workspace || ws_bytes < p->ws_bytes) return QLIN_ERR_WORKSPACE;
+    return make_plan(fmt, M, N, K, *c, fused, p);
+}
+
+static qlin_status check_workspace(const Plan &p, void *workspace, size_t ws_bytes) {
+    if (p.ws_bytes > 0) {
+        if (!workspace || ws_bytes < p.ws_bytes) return QLIN_ERR_WORKSPACE;
         if (!aligned16(workspace)) return QLIN_ERR_ALIGNMENT;
     }
     return QLIN_OK;
+}
+
+static qlin_status check_gemm(qlin_format fmt, int M, int N, int K, const float *x_scales,
+                              const void *wq, const float *w_scales, void *y,
+                              qlin_out_type out_type, const qlin_config *cfg, void *workspace,
+                              size_t ws_bytes, bool fused, qlin_config *c, Plan *p) {
+    qlin_status st = check_gemm_args(fmt, M, N, K, x_scales, wq, w_scales, y, out_type, cfg, fused, c, p);
+    if (st != QLIN_OK) return st;
+    return check_workspace(*p, workspace, ws_bytes);
 }
 
 static GemmLaunch launch_args(const Plan &p, int M, int N, int K, const void *wq,
@@ -306,27 +317,33 @@ qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, cons
                                   static_cast<hipStream_t>(stream)));
 }
 
-qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
-                        float *x_scales, const void *wq, const float *w_scales, void *y,
-                        qlin_out_type out_type, const qlin_config *cfg, void *workspace,
-                        size_t ws_bytes, void *stream) {
-    qlin_config c;
-    Plan p;
-    qlin_status st = check_gemm(fmt, M, N, K, x_scales, wq, w_scales, y, out_type, cfg, workspace,
-                                ws_bytes, true, &c, &p);
+// Validates a qlin_linear call (everything but the workspace) and plans it:
+// fills *c and *p, with the in-kernel quantization turned off where the
+// tile's rows of x are too far apart for its 32-bit offsets.
+static qlin_status plan_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx,
+                               void *xq, const float *x_scales, const void *wq, const float *w_scales,
+                               void *y, qlin_out_type out_type, const qlin_config *cfg, qlin_config *c,
+                               Plan *p) {
+    qlin_status st = check_gemm_args(fmt, M, N, K, x_scales, wq, w_scales, y, out_type, cfg, true, c, p);
     if (st != QLIN_OK) return st;
     if (!x || !xq) return QLIN_ERR_INVALID_ARG;
     if (ldx < K || ldx % 8 != 0) return QLIN_ERR_ALIGNMENT;
     if (!aligned16(x) || !aligned16(xq)) return QLIN_ERR_ALIGNMENT;
-    if (M == 0) return QLIN_OK;
     // the in-kernel quantization addresses the tile's rows of x with 32-bit
     // byte offsets; a very wide row stride takes the two-kernel path
-    if (p.fuse && ((int64_t)((M < c.tile_m ? M : c.tile_m) - 1) * ldx + K) * 2 >= ((int64_t)1 << 31)) {
-        c.fuse_quant = 0;
-        st = make_plan(fmt, M, N, K, c, true, &p);
+    if (p->fuse && ((int64_t)((M < c->tile_m ? M : c->tile_m) - 1) * ldx + K) * 2 >= ((int64_t)1 << 31)) {
+        c->fuse_quant = 0;
+        st = make_plan(fmt, M, N, K, *c, true, p);
         if (st != QLIN_OK) return st;
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return QLIN_OK;
+}
+
+// Enqueues a planned qlin_linear call (quantize + GEMM, or the fused GEMM).
+static qlin_status run_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
+                              float *x_scales, const void *wq, const float *w_scales, void *y,
+                              qlin_out_type out_type, const qlin_config &c, const Plan &p, void *workspace,
+                              hipStream_t s) {
     GemmLaunch g = launch_args(p, M, N, K, wq, w_scales, y, out_type, workspace);
     if (p.fuse) {
         g.x = static_cast<const uint16_t *>(x);
@@ -334,12 +351,45 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
         g.xq_out = static_cast<uint8_t *>(xq);
         g.xs_out = x_scales;
     } else {
-        st = hip_status(launch_quant_act(fmt, M, K, x, ldx, xq, x_scales, s));
+        qlin_status st = hip_status(launch_quant_act(fmt, M, K, x, ldx, xq, x_scales, s));
         if (st != QLIN_OK) return st;
         g.xq = static_cast<const uint8_t *>(xq);
         g.xs = x_scales;
     }
     return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, p.xc, g, p.lds_bytes, s));
+}
+
+qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
+                        float *x_scales, const void *wq, const float *w_scales, void *y,
+                        qlin_out_type out_type, const qlin_config *cfg, void *workspace,
+                        size_t ws_bytes, void *stream) {
+    qlin_config c;
+    Plan p;
+    qlin_status st = plan_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, cfg, &c, &p);
+    if (st != QLIN_OK) return st;
+    st = check_workspace(p, workspace, ws_bytes);
+    if (st != QLIN_OK) return st;
+    if (M == 0) return QLIN_OK;
+    return run_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, c, p, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+qlin_status qlin_linear_scratch(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
+                                float *x_scales, const void *wq, const float *w_scales, void *y,
+                                qlin_out_type out_type, const qlin_config *cfg, void *stream) {
+    qlin_config c;
+    Plan p;
+    qlin_status st = plan_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, cfg, &c, &p);
+    if (st != QLIN_OK) return st;
+    if (p.ws_bytes > kScratchBytes) return QLIN_ERR_WORKSPACE;
+    if (M == 0) return QLIN_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (p.ws_bytes > 0) {
+        st = hip_status(static_scratch(s, &ws));
+        if (st != QLIN_OK) return st;
+    }
+    return run_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, c, p, ws, s);
 }
 
 // ---------------------------------------------------------------- grouped

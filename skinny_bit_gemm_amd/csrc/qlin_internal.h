@@ -15,6 +15,8 @@ constexpr int kGroup = 128;          // K block: one fp8 MFMA, one 1x128 scale g
 constexpr int kMaxWaves = 8;         // waves per workgroup
 constexpr int kLdsBudget = 78 * 1024; // bytes of LDS a GEMM workgroup may use (two fit a CU)
 constexpr int kMaxSplit = 64;
+// size of the static split-K workspace of qlin_linear_scratch (per GPU)
+constexpr size_t kScratchBytes = QLIN_SCRATCH_BYTES;
 
 // Everything a GEMM launch needs, resolved on the host.
 struct GemmLaunch {
@@ -86,5 +88,8 @@ hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, 
 hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, int xc, const GemmLaunch &g,
                        size_t lds_bytes, hipStream_t s);
 bool gemm_variant_exists(int fmt, int tile_m, int nr, int xc);
+// this device's static scratch array (kScratchBytes, zero between calls);
+// see qlin_linear_scratch
+hipError_t static_scratch(hipStream_t s, void **out);
 
 }  // namespace qlin

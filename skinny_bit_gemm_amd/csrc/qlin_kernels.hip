@@ -8,6 +8,8 @@
 //
 // Data layout (all row-major): activations x bf16 [M][ldx], codes xq [M][K],
 // weights wq [N][K] (K contiguous, as a torch Linear weight), output y [M][N].
+#include <mutex>
+
 #include "qlin_gemm.h"
 
 namespace qlin {
@@ -192,6 +194,67 @@ hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, 
         hipLaunchKernelGGL(quant_channel_kernel<FMT_FP8>, dim3(N), dim3(256), 0, s, w, K, q, ws);
     }
     return hipGetLastError();
+}
+
+// ------------------------------------------------------ static scratch space
+
+// The split-K workspace of qlin_linear_scratch: a file-scope device array
+// that each GPU holds for the life of the process (every call on a GPU
+// shares it).  In host code its name is only a stand-in for the symbol; the
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+    std::once_flag once;
+    hipError_t status = hipSuccess;
+    void *ptr = nullptr;        // this device's address of `scratch`
+    bool zeroed = false;        // a zero fill ran eagerly (outside capture)
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4 *p, size_t n16) {
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace
+
+// Device address of this device's scratch array, and makes sure it holds
+// zeros before the first kernel that uses it: a fill kernel on `s` (not a
+// memset node, which graph replays have been seen to mishandle).  A call
+// made while `s` is being captured records the fill in the graph (so every
+// replay starts from zeros) and leaves it to the next eager call to fill it
+// once outside the graph.  After that the kernels keep it zero.
+hipError_t static_scratch(hipStream_t s, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot]() {
+        slot.status = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+        if (slot.status == hipSuccess && slot.ptr == nullptr) slot.status = hipErrorInvalidSymbol;
+    });
+    if (slot.status != hipSuccess) return slot.status;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!slot.zeroed) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(s, &cs);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(512), dim3(256), 0, s, static_cast<uint4 *>(slot.ptr),
+                           kScratchBytes / 16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (cs == hipStreamCaptureStatusNone) slot.zeroed = true;
+    }
+    *out = slot.ptr;
+    return hipSuccess;
 }
 
 bool gemm_variant_exists(int fmt, int tile_m, int nr, int xc) {

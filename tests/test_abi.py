@@ -86,6 +86,27 @@ def test_gemm_rejects_bad_arguments():
     assert gemm(fmt=I8, K=133_120 + 128) == ESHAPE  # int32 sums could overflow
 
 
+def test_linear_scratch_checks_before_any_hip_call():
+    """qlin_linear_scratch validates like qlin_linear and rejects a schedule
+    whose workspace does not fit the static scratch array; M = 0 enqueues
+    nothing."""
+    def call(fmt=FP8, M=4, N=256, K=512, x=A, ldx=512, y=A, cfg=None):
+        return q.qlin_linear_scratch(fmt, M, N, K, x, ldx, A, A, A, A, y, 0, cfg, stream=0,
+                                     raise_on_error=False)
+    assert call(fmt=9) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(y=A + 8) == EALIGN
+    assert call(ldx=500) == EALIGN
+    assert call(K=520, ldx=520) == ESHAPE
+    assert call(cfg=q.make_config(split_k=0)) == EINVAL
+    big = q.make_config(1, 16, 32, 64, 4, 2, 0, 0)
+    need = q.qlin_workspace_bytes(FP8, 32, 8192, 8192, big)
+    assert need > q.QLIN_SCRATCH_BYTES
+    assert call(M=32, N=8192, K=8192, ldx=8192, cfg=big) == EWS
+    assert call(M=0, N=8192, K=8192, ldx=8192, cfg=big) == OK   # nothing to compute
+    assert call(M=0) == OK
+
+
 def test_gemm_rejects_bad_configs():
     bad = [q.make_config(swap_ab=2), q.make_config(split_k=0), q.make_config(split_k=65),
            q.make_config(tile_m=8), q.make_config(waves=0, k_waves=1),
