@@ -4,9 +4,11 @@ A step is one pass of the hot path over one batch of synthetic inputs: for
 every token count M of the workload and every linear layer of the model, the
 whole quantized linear (qlin_linear: activation quantization and GEMM, as one
 fused kernel or two, per the selection table), replayed from a hipGraph
-captured once (the decode path runs only under graph replay).  Weights live in HBM as
-R distinct rotating copies (>= 1 GiB in total) so the 256 MiB Infinity Cache
-cannot serve them; activations, scales and outputs are resident too.
+captured once (the decode path runs only under graph replay).  Weights are
+quantized and packed offline (qlin_quantize_weight, qlin_pack_weight) and
+live in HBM as R distinct rotating copies (>= 1 GiB in total) so the 256 MiB
+Infinity Cache cannot serve them; activations, scales and outputs are
+resident too.
 
 Prints one JSON line: whole-step throughput (algorithmic bytes / time), the
 GEMM roofline entry (its algorithmic bytes over its measured duration, from
@@ -79,6 +81,8 @@ class Linear:
         import skinny_bit_gemm_amd as q
         import workloads as wl
         self.fmt, self.M, self.N, self.K = fmt, M, layer.N, layer.K
+        # the weights are in the packed layout (offline preparation)
+        self.call_fmt = fmt | q.QLIN_PACKED_WEIGHTS
         self.name = layer.name
         x = wl.activations(fmt, layer.N, layer.K, M)
         self.x = torch.from_numpy(x.view("int16")).to(dev)
@@ -96,13 +100,13 @@ class Linear:
     def layer(self, stream, wq=None):
         """The whole decode linear: quantize + GEMM (one or two kernels, as tuned)."""
         import skinny_bit_gemm_amd as q
-        q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs,
+        q.qlin_linear(self.call_fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs,
                       self.wq if wq is None else wq, self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work,
                       stream=stream)
 
     def gemm(self, stream, wq=None):
         import skinny_bit_gemm_amd as q
-        q.qlin_gemm(self.fmt, self.M, self.N, self.K, self.xq, self.xs, self.wq if wq is None else wq,
+        q.qlin_gemm(self.call_fmt, self.M, self.N, self.K, self.xq, self.xs, self.wq if wq is None else wq,
                     self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work, stream=stream)
 
     @property
@@ -257,11 +261,7 @@ def crossover_sweep(path, fmts, Ms):
         for fmt in fmts:
             for L in wl.DENSE_8B:
                 N, K = L.N, L.K
-                w = torch.from_numpy(wl.weights(fmt, N, K)).to(dev)
-                wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
-                ws = torch.empty(q.scales_shape(fmt, N, K, True), dtype=torch.float32, device=dev)
-                q.qlin_quantize_weight(fmt, N, K, w, wq, ws, stream=st)
-                del w
+                wq, ws = prepare_weights(fmt, L, dev)
                 R = max(2, -(-(1 << 30) // (N * K)))
                 copies = [wq.clone() for _ in range(R)]
                 for M in Ms:
@@ -274,8 +274,8 @@ def crossover_sweep(path, fmts, Ms):
                         cfg = c if c is not None else q.qlin_select_variant(fmt, M, N, K)
                         work = torch.zeros(max(256, q.qlin_workspace_bytes(fmt, M, N, K, cfg)),
                                            dtype=torch.uint8, device=dev)
-                        run = lambda: [q.qlin_gemm(fmt, M, N, K, xq, xs, wc, ws, y, q.QLIN_OUT_BF16, cfg, work,
-                                                   stream=st) for wc in copies]
+                        run = lambda: [q.qlin_gemm(fmt | q.QLIN_PACKED_WEIGHTS, M, N, K, xq, xs, wc, ws, y,
+                                                   q.QLIN_OUT_BF16, cfg, work, stream=st) for wc in copies]
                         run()
                         g = capture(st, run)
                         warm_graph(g, st)
@@ -370,6 +370,12 @@ def moe_bench(path, fmts, Ts, layers=None, schedules=None):
                     w = torch.randn((N, K), generator=gen, device=dev) * 0.02
                     q.qlin_quantize_weight(fmt, N, K, w, wq[e], ws[e], stream=st)
                 del w
+                # the experts' codes in the packed layout, one matrix after another
+                wpk = torch.empty((E, q.qlin_packed_weight_bytes(N, K)), dtype=torch.uint8, device=dev)
+                q.qlin_pack_weight(E, N, K, wq, wpk, stream=st)
+                torch.cuda.synchronize()
+                wq = wpk
+                fmt_w = fmt | q.QLIN_PACKED_WEIGHTS
                 C = max(2, -(-(2 << 30) // (E * N * K)))
                 copies = [wq] + [wq.clone() for _ in range(C - 1)]
                 for T in Ts:
@@ -392,7 +398,7 @@ def moe_bench(path, fmts, Ts, layers=None, schedules=None):
                         cfg = c if c is not None else q.qlin_grouped_select_variant(fmt, E, N, K, T)
                         nb = q.qlin_grouped_workspace_bytes(fmt, E, N, K, total, T, cfg)
                         work = torch.zeros(max(256, nb), dtype=torch.uint8, device=dev)
-                        us = timed(lambda: [q.qlin_grouped_gemm(fmt, E, N, K, offs[i], total, T, xq, xs,
+                        us = timed(lambda: [q.qlin_grouped_gemm(fmt_w, E, N, K, offs[i], total, T, xq, xs,
                                                                 copies[i % C], ws, y, q.QLIN_OUT_BF16, cfg, work,
                                                                 stream=st) for i in range(R)], R)
                         rows_out.append(dict(point, schedule=name, cfg=cfg.as_dict(), us=round(us, 3),
@@ -418,7 +424,7 @@ def moe_bench(path, fmts, Ts, layers=None, schedules=None):
 
                     def per_expert():
                         for i, lo, hi, e, cfg, _ in launches:
-                            q.qlin_gemm(fmt, hi - lo, N, K, xq[lo:hi], xs[lo:hi],
+                            q.qlin_gemm(fmt_w, hi - lo, N, K, xq[lo:hi], xs[lo:hi],
                                         copies[i % C][e], ws[e], y[lo:hi], q.QLIN_OUT_BF16, cfg, work, stream=st)
                     us = timed(per_expert, R)
                     rows_out.append(dict(point, schedule="per_expert_launches", cfg=None, us=round(us, 3),
@@ -440,6 +446,24 @@ def moe_bench(path, fmts, Ts, layers=None, schedules=None):
             "geomean_rule_GBps": geomean("rule"), "geomean_per_expert_GBps": geomean("per_expert_launches")}
 
 
+def prepare_weights(fmt, L, dev):
+    """Offline weight preparation of one layer: quantize the N(0, 0.02)
+    master weights on the GPU, then reorder the codes into the packed layout
+    the kernels stream fastest.  Returns (packed codes, scales)."""
+    import torch
+    import skinny_bit_gemm_amd as q
+    import workloads as wl
+    w = torch.from_numpy(wl.weights(fmt, L.N, L.K)).to(dev)
+    wq = torch.empty((L.N, L.K), dtype=torch.uint8, device=dev)
+    ws = torch.empty(q.scales_shape(fmt, L.N, L.K, True), dtype=torch.float32, device=dev)
+    q.qlin_quantize_weight(fmt, L.N, L.K, w, wq, ws)
+    del w
+    wp = torch.empty(q.qlin_packed_weight_bytes(L.N, L.K), dtype=torch.uint8, device=dev)
+    q.qlin_pack_weight(1, L.N, L.K, wq, wp)
+    torch.cuda.synchronize()
+    return wp, ws
+
+
 def run_workload(name, steps, warmup, detail=False, gemm_only_steps=None, floors=None):
     """Times one workload's step: every (M, layer) linear of it, replayed
     from hipGraphs over rotating weight copies; then the step's GEMM kernels
@@ -454,15 +478,11 @@ def run_workload(name, steps, warmup, detail=False, gemm_only_steps=None, floors
 
     fmt, layers, Ms = wl.WORKLOADS[name]
     dev = torch.device("cuda:0")
-    # quantized weights (GPU quantizer, offline and untimed), then rotating copies
+    # quantized and packed weights (GPU quantizer and packer, offline and
+    # untimed), then rotating copies
     base = {}
     for L in layers:
-        w = torch.from_numpy(wl.weights(fmt, L.N, L.K)).to(dev)
-        wq = torch.empty((L.N, L.K), dtype=torch.uint8, device=dev)
-        ws = torch.empty(q.scales_shape(fmt, L.N, L.K, True), dtype=torch.float32, device=dev)
-        q.qlin_quantize_weight(fmt, L.N, L.K, w, wq, ws)
-        base[L.name] = (wq, ws)
-        del w
+        base[L.name] = prepare_weights(fmt, L, dev)
     torch.cuda.synchronize()
     step_wbytes = sum(L.N * L.K for L in layers) * len(Ms)
     n_sets = max(2, -(-(1 << 30) // step_wbytes))

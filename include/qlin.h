@@ -58,6 +58,13 @@ typedef enum {
     QLIN_BLOCK_FP8 = 2
 } qlin_format;
 
+/* Weight layout flag: OR-ed into the format argument of qlin_gemm,
+ * qlin_linear, qlin_linear_scratch and qlin_grouped_gemm (and accepted,
+ * without effect, by the schedule queries), it says that wq holds the codes
+ * in the packed layout of qlin_pack_weight instead of [N, K] row-major.
+ * Results are identical; only the memory traffic pattern changes. */
+#define QLIN_PACKED_WEIGHTS 0x100
+
 typedef enum {
     QLIN_OUT_BF16 = 0,    /* y: bf16 [M,N], the product                     */
     QLIN_OUT_F32_ACC = 1, /* y: fp32 [M,N], scaled sums before bf16 rounding */
@@ -137,9 +144,27 @@ qlin_status qlin_quantize_act(qlin_format fmt, int M, int K, const void *x, int6
 qlin_status qlin_quantize_weight(qlin_format fmt, int N, int K, const float *w, void *wq,
                                  float *w_scales, void *stream);
 
+/* Packed weight layout (offline preparation, like the quantization): the
+ * codes of each 16-row x 128-K block of W become 2 KiB of consecutive
+ * bytes, in the order in which the GEMM kernels' 64-lane waves hold them,
+ * so that every weight load of a wave reads 1 KiB of consecutive memory.
+ * For 16-row group s, K block kb (nkb = ceil(K / 128) blocks), half h and
+ * lane l, the 16 bytes at offset 1024 ((s nkb + kb) 2 + h) + 16 l are codes
+ * [16 s + l % 16][128 kb + 32 (l / 16) + 16 h + 0 .. 15] of the row-major
+ * matrix, zeros past K.  The product ("Building a High-Performance and
+ * Portable vLLM Linear Backend with Helion", section "Kernel
+ * Implementation") does not depend on how the weights are stored.
+ *   batch      matrices back to back (a grouped layer's experts): wq is
+ *              [batch][N][K], wq_packed [batch][qlin_packed_weight_bytes]
+ *   N, K       multiples of 16
+ * wq and wq_packed must not overlap.  batch 0 enqueues nothing. */
+qlin_status qlin_packed_weight_bytes(int N, int K, size_t *bytes);
+qlin_status qlin_pack_weight(int batch, int N, int K, const void *wq, void *wq_packed, void *stream);
+
 /* The quantized GEMM y = dequant(xq . wq^T).
  *   xq, x_scales  as produced by qlin_quantize_act
- *   wq, w_scales  as produced by qlin_quantize_weight ([N,K] row-major)
+ *   wq, w_scales  as produced by qlin_quantize_weight ([N,K] row-major), or
+ *                 wq packed by qlin_pack_weight with QLIN_PACKED_WEIGHTS in fmt
  *   y             [M, N] row-major of the out_type's element type
  *   cfg           NULL: look the schedule up with qlin_select_variant;
  *                 otherwise that schedule is forced (it must be valid)
@@ -228,7 +253,8 @@ qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qli
  *                  top-k routing, the token count bounds every group.
  *   xq, x_scales   [total_rows, K] codes and their scales (qlin_quantize_act
  *                  layouts), rows grouped by group
- *   wq, w_scales   [groups][N][K] codes and [groups][N] (or
+ *   wq, w_scales   [groups][N][K] codes (or [groups] packed matrices with
+ *                  QLIN_PACKED_WEIGHTS) and [groups][N] (or
  *                  [groups][N/128][K/128] for QLIN_BLOCK_FP8) scales
  *   y              [total_rows, N]
  *   cfg            NULL: qlin_grouped_select_variant's rule; otherwise

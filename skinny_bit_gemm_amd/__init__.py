@@ -32,8 +32,10 @@ EXPORTS = (
     "qlin_table_entries", "qlin_graph_begin", "qlin_graph_end", "qlin_graph_launch",
     "qlin_graph_destroy", "qlin_status_str", "qlin_abi_version", "qlin_last_hip_error",
     "qlin_grouped_gemm", "qlin_grouped_select_variant", "qlin_grouped_workspace_bytes",
-    "qlin_linear_scratch",
+    "qlin_linear_scratch", "qlin_packed_weight_bytes", "qlin_pack_weight",
 )
+# format flag: the weight codes are in the packed layout of qlin_pack_weight
+QLIN_PACKED_WEIGHTS = 0x100
 # bytes of the static split-K workspace of qlin_linear_scratch (per GPU)
 QLIN_SCRATCH_BYTES = 8 << 20
 
@@ -94,6 +96,8 @@ def lib():
                                   ctypes.POINTER(qlin_config), _P, _SZ, _P]
         L.qlin_linear_scratch.argtypes = [_I, _I, _I, _I, _P, _I64, _P, _P, _P, _P, _P, _I,
                                           ctypes.POINTER(qlin_config), _P]
+        L.qlin_packed_weight_bytes.argtypes = [_I, _I, ctypes.POINTER(_SZ)]
+        L.qlin_pack_weight.argtypes = [_I, _I, _I, _P, _P, _P]
         L.qlin_select_variant.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config)]
         L.qlin_workspace_bytes.argtypes = [_I, _I, _I, _I, ctypes.POINTER(qlin_config),
                                            ctypes.POINTER(_SZ)]
@@ -183,6 +187,17 @@ def qlin_linear_scratch(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out
     st = lib().qlin_linear_scratch(fmt, M, N, K, _ptr(x), ldx, _ptr(xq), _ptr(x_scales), _ptr(wq),
                                    _ptr(w_scales), _ptr(y), out_type, cptr, _stream(stream))
     return _check(st, "qlin_linear_scratch", raise_on_error)
+
+
+def qlin_packed_weight_bytes(N, K) -> int:
+    out = _SZ(0)
+    _check(lib().qlin_packed_weight_bytes(N, K, ctypes.byref(out)), "qlin_packed_weight_bytes", True)
+    return int(out.value)
+
+
+def qlin_pack_weight(batch, N, K, wq, wq_packed, stream=None, raise_on_error=True):
+    st = lib().qlin_pack_weight(batch, N, K, _ptr(wq), _ptr(wq_packed), _stream(stream))
+    return _check(st, "qlin_pack_weight", raise_on_error)
 
 
 def qlin_select_variant(fmt, M, N, K) -> qlin_config:

@@ -32,6 +32,11 @@ qlin_status shape_ok(int fmt, int M, int N, int K) {
     return QLIN_OK;
 }
 
+// The format argument of the GEMM calls: a number format, optionally with
+// QLIN_PACKED_WEIGHTS (the weight codes' layout) OR-ed in.
+qlin_format base_format(qlin_format f) { return (qlin_format)((int)f & ~QLIN_PACKED_WEIGHTS); }
+bool packed_weights(qlin_format f) { return ((int)f & QLIN_PACKED_WEIGHTS) != 0; }
+
 qlin_status hip_status(hipError_t e) {
     if (e == hipSuccess) return QLIN_OK;
     g_last_hip_error = (int)e;
@@ -204,6 +209,7 @@ qlin_status qlin_quantize_weight(qlin_format fmt, int N, int K, const float *w, 
 }
 
 qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qlin_config *cfg) {
+    fmt = base_format(fmt);   // the weight layout does not change the schedule
     if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
     qlin_status st = shape_ok(fmt, M, N, K);
     if (st != QLIN_OK) return st;
@@ -213,6 +219,7 @@ qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qli
 }
 
 qlin_status qlin_select_variant(qlin_format fmt, int M, int N, int K, qlin_config *out) {
+    fmt = base_format(fmt);   // the weight layout does not change the schedule
     if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
     if (!out) return QLIN_ERR_INVALID_ARG;
     qlin_status st = shape_ok(fmt, M, N, K);
@@ -222,6 +229,7 @@ qlin_status qlin_select_variant(qlin_format fmt, int M, int N, int K, qlin_confi
 
 qlin_status qlin_workspace_bytes(qlin_format fmt, int M, int N, int K, const qlin_config *cfg,
                                  size_t *bytes) {
+    fmt = base_format(fmt);   // the weight layout does not change the schedule
     if (!fmt_ok(fmt) || !bytes) return QLIN_ERR_INVALID_ARG;
     qlin_status st = shape_ok(fmt, M, N, K);
     if (st != QLIN_OK) return st;
@@ -272,10 +280,12 @@ static qlin_status check_gemm(qlin_format fmt, int M, int N, int K, const float 
     return check_workspace(*p, workspace, ws_bytes);
 }
 
-static GemmLaunch launch_args(const Plan &p, int M, int N, int K, const void *wq,
+static GemmLaunch launch_args(const Plan &p, int M, int N, int K, const void *wq, bool w_packed,
                               const float *w_scales, void *y, qlin_out_type out_type,
                               void *workspace) {
     GemmLaunch g = {};
+    g.w_packed = w_packed;
+    g.w_group_stride = w_packed ? packed_weight_bytes(N, K) : (int64_t)N * K;
     g.wq = static_cast<const uint8_t *>(wq);
     g.wsc = w_scales;
     g.y = y;
@@ -302,6 +312,8 @@ static GemmLaunch launch_args(const Plan &p, int M, int N, int K, const void *wq
 qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, const float *x_scales,
                       const void *wq, const float *w_scales, void *y, qlin_out_type out_type,
                       const qlin_config *cfg, void *workspace, size_t ws_bytes, void *stream) {
+    const bool wpk = packed_weights(fmt);
+    fmt = base_format(fmt);
     qlin_config c;
     Plan p;
     qlin_status st = check_gemm(fmt, M, N, K, x_scales, wq, w_scales, y, out_type, cfg, workspace,
@@ -310,7 +322,7 @@ qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, cons
     if (!xq) return QLIN_ERR_INVALID_ARG;
     if (!aligned16(xq)) return QLIN_ERR_ALIGNMENT;
     if (M == 0) return QLIN_OK;
-    GemmLaunch g = launch_args(p, M, N, K, wq, w_scales, y, out_type, workspace);
+    GemmLaunch g = launch_args(p, M, N, K, wq, wpk, w_scales, y, out_type, workspace);
     g.xq = static_cast<const uint8_t *>(xq);
     g.xs = x_scales;
     return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, 0, g, p.lds_bytes,
@@ -341,10 +353,10 @@ static qlin_status plan_linear(qlin_format fmt, int M, int N, int K, const void 
 
 // Enqueues a planned qlin_linear call (quantize + GEMM, or the fused GEMM).
 static qlin_status run_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
-                              float *x_scales, const void *wq, const float *w_scales, void *y,
+                              float *x_scales, const void *wq, bool w_packed, const float *w_scales, void *y,
                               qlin_out_type out_type, const qlin_config &c, const Plan &p, void *workspace,
                               hipStream_t s) {
-    GemmLaunch g = launch_args(p, M, N, K, wq, w_scales, y, out_type, workspace);
+    GemmLaunch g = launch_args(p, M, N, K, wq, w_packed, w_scales, y, out_type, workspace);
     if (p.fuse) {
         g.x = static_cast<const uint16_t *>(x);
         g.ldx = ldx;
@@ -363,6 +375,8 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
                         float *x_scales, const void *wq, const float *w_scales, void *y,
                         qlin_out_type out_type, const qlin_config *cfg, void *workspace,
                         size_t ws_bytes, void *stream) {
+    const bool wpk = packed_weights(fmt);
+    fmt = base_format(fmt);
     qlin_config c;
     Plan p;
     qlin_status st = plan_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, cfg, &c, &p);
@@ -370,13 +384,15 @@ qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int
     st = check_workspace(p, workspace, ws_bytes);
     if (st != QLIN_OK) return st;
     if (M == 0) return QLIN_OK;
-    return run_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, c, p, workspace,
+    return run_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, wpk, w_scales, y, out_type, c, p, workspace,
                       static_cast<hipStream_t>(stream));
 }
 
 qlin_status qlin_linear_scratch(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
                                 float *x_scales, const void *wq, const float *w_scales, void *y,
                                 qlin_out_type out_type, const qlin_config *cfg, void *stream) {
+    const bool wpk = packed_weights(fmt);
+    fmt = base_format(fmt);
     qlin_config c;
     Plan p;
     qlin_status st = plan_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, cfg, &c, &p);
@@ -389,7 +405,7 @@ qlin_status qlin_linear_scratch(qlin_format fmt, int M, int N, int K, const void
         st = hip_status(static_scratch(s, &ws));
         if (st != QLIN_OK) return st;
     }
-    return run_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, w_scales, y, out_type, c, p, ws, s);
+    return run_linear(fmt, M, N, K, x, ldx, xq, x_scales, wq, wpk, w_scales, y, out_type, c, p, ws, s);
 }
 
 // ---------------------------------------------------------------- grouped
@@ -454,6 +470,7 @@ static qlin_status grouped_plan(qlin_format fmt, int groups, int N, int K, int t
 
 qlin_status qlin_grouped_select_variant(qlin_format fmt, int groups, int N, int K, int max_group_rows,
                                         qlin_config *out) {
+    fmt = base_format(fmt);
     if (!out) return QLIN_ERR_INVALID_ARG;
     Plan p;
     return grouped_plan(fmt, groups, N, K, 0, max_group_rows, nullptr, out, &p);
@@ -461,6 +478,7 @@ qlin_status qlin_grouped_select_variant(qlin_format fmt, int groups, int N, int 
 
 qlin_status qlin_grouped_workspace_bytes(qlin_format fmt, int groups, int N, int K, int total_rows,
                                          int max_group_rows, const qlin_config *cfg, size_t *bytes) {
+    fmt = base_format(fmt);
     if (!bytes) return QLIN_ERR_INVALID_ARG;
     qlin_config c;
     Plan p;
@@ -474,6 +492,8 @@ qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const i
                               int total_rows, int max_group_rows, const void *xq, const float *x_scales,
                               const void *wq, const float *w_scales, void *y, qlin_out_type out_type,
                               const qlin_config *cfg, void *workspace, size_t ws_bytes, void *stream) {
+    const bool wpk = packed_weights(fmt);
+    fmt = base_format(fmt);
     if (out_type != QLIN_OUT_BF16 && out_type != QLIN_OUT_F32_ACC && out_type != QLIN_OUT_I32_ACC)
         return QLIN_ERR_INVALID_ARG;
     if (out_type == QLIN_OUT_I32_ACC && fmt != QLIN_W8A8_INT8) return QLIN_ERR_INVALID_ARG;
@@ -488,7 +508,7 @@ qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const i
     if (p.ws_bytes && (!workspace || ws_bytes < p.ws_bytes)) return QLIN_ERR_WORKSPACE;
     if (p.ws_bytes && !aligned16(workspace)) return QLIN_ERR_ALIGNMENT;
     if (total_rows == 0) return QLIN_OK;
-    GemmLaunch g = launch_args(p, total_rows, N, K, wq, w_scales, y, out_type, workspace);
+    GemmLaunch g = launch_args(p, total_rows, N, K, wq, wpk, w_scales, y, out_type, workspace);
     g.xq = static_cast<const uint8_t *>(xq);
     g.xs = x_scales;
     g.group_off = group_offsets;
@@ -497,6 +517,22 @@ qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const i
     g.m_tiles = p.m_tiles;   // grid y
     return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, 0, g, p.lds_bytes,
                                   static_cast<hipStream_t>(stream)));
+}
+
+qlin_status qlin_packed_weight_bytes(int N, int K, size_t *bytes) {
+    if (!bytes) return QLIN_ERR_INVALID_ARG;
+    if (N < 16 || N > kMaxDim || K < 16 || K > kMaxDim || N % 16 != 0 || K % 16 != 0) return QLIN_ERR_SHAPE;
+    *bytes = (size_t)packed_weight_bytes(N, K);
+    return QLIN_OK;
+}
+
+qlin_status qlin_pack_weight(int batch, int N, int K, const void *wq, void *wq_packed, void *stream) {
+    if (batch < 0 || batch > 65535) return QLIN_ERR_SHAPE;
+    if (N < 16 || N > kMaxDim || K < 16 || K > kMaxDim || N % 16 != 0 || K % 16 != 0) return QLIN_ERR_SHAPE;
+    if (!wq || !wq_packed) return QLIN_ERR_INVALID_ARG;
+    if (!aligned16(wq) || !aligned16(wq_packed)) return QLIN_ERR_ALIGNMENT;
+    if (batch == 0) return QLIN_OK;
+    return hip_status(launch_pack_weight(batch, N, K, wq, wq_packed, static_cast<hipStream_t>(stream)));
 }
 
 struct qlin_graph_s {

@@ -141,20 +141,25 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off)
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// 32 bytes of the lane's weight row in K block kb (lane_off = row * K + 32 *
-// quarter, in a resource that covers one sub-tile of 16 or 8 rows; k = the lane's
-// first K index).  The block's offset is a scalar operand, so a slot costs
-// no address registers.  A 16-byte half at or past K (in a partial last
-// block), or a dead slot, uses an out-of-range lane offset, so every lane
+// 32 bytes of the lane's weight row in K block kb: bytes 32 quarter ..
+// 32 quarter + 31 of the block, as two 16-byte halves.  Row-major codes:
+// lane_off = row * K + 32 * quarter in a resource that covers the sub-tile's
+// rows, halves 16 bytes apart, blocks 128 bytes apart; a half at or past K
+// (in a partial last block) is read out of range.  Packed codes: lane_off =
+// 16 (16 quarter + row) in a resource that covers the sub-tile's 16-row
+// group, halves 1 KiB apart, blocks 2 KiB apart, the tail of K already
+// zero.  The block's offset is a scalar operand, so a slot costs no address
+// registers; a dead slot uses an out-of-range lane offset, so every lane
 // issues the same two loads per block and nothing has to be masked after
 // the data arrives.
 __device__ __forceinline__ v8i load_w(__amdgpu_buffer_rsrc_t rs, uint32_t lane_off, int kb, int k,
-                                      int K, bool live) {
-    const int boff = __builtin_amdgcn_readfirstlane(kb * kGroup);
-    const uint32_t lo_off = live && k < K ? lane_off : kOutOfRange;
-    const uint32_t hi_off = live && k + 16 < K ? lane_off : kOutOfRange;
+                                      int K, bool live, bool packed) {
+    const int boff = __builtin_amdgcn_readfirstlane(kb * (packed ? kPackBlock : kGroup));
+    const int hoff = packed ? kPackBlock / 2 : 16;
+    const uint32_t lo_off = live && (packed || k < K) ? lane_off : kOutOfRange;
+    const uint32_t hi_off = live && (packed || k + 16 < K) ? lane_off : kOutOfRange;
     const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(rs, lo_off, boff, 0);
-    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rs, hi_off, boff + 16, 0);
+    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rs, hi_off, boff + hoff, 0);
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         g.xq += (int64_t)lo * g.K;
         g.xs += (int64_t)lo * (FMT == FMT_BLOCK ? Gk : 1);
         g.y = static_cast<uint8_t *>(g.y) + (int64_t)lo * g.N * (g.out_type == QLIN_OUT_BF16 ? 2 : 4);
-        g.wq += (int64_t)e * g.N * g.K;
+        g.wq += (int64_t)e * g.w_group_stride;
         g.wsc += (int64_t)e * (FMT == FMT_BLOCK ? (int64_t)(g.N / kGroup) * Gk : g.N);
         if (g.acc_ws) g.acc_ws = static_cast<uint8_t *>(g.acc_ws) + (int64_t)lo * g.N * (g.packed ? 8 : 4);
         g.M = hi - lo;
@@ -381,15 +386,27 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
 
     int nsub[NR];
     __amdgpu_buffer_rsrc_t wrs[NR];
+    const bool wpk = g.w_packed != 0;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         nsub[r] = n_tile0 + (nw * NR + r) * SR;
         // sub-tiles past N get an empty resource: their loads return zeros
-        // (as do rows SR .. 15 of a sub-tile: past the resource's end)
         const int base = min(nsub[r], N - SR);
-        wrs[r] = buffer_rsrc(g.wq + (int64_t)base * K, nsub[r] < N ? (uint32_t)SR * K : 0u);
+        if (wpk) {
+            // packed: the 16-row group's 2 KiB blocks; an 8-row sub-tile that
+            // is the group's second half starts 128 bytes into each 1 KiB
+            // half-block (its rows are lanes 8 .. 15 of every quarter)
+            const int half = (base >> 3) & 1;
+            wrs[r] = buffer_rsrc(g.wq + (int64_t)(base >> 4) * g.nkb * kPackBlock + half * 128,
+                                 nsub[r] < N ? (uint32_t)(g.nkb * kPackBlock - half * 128) : 0u);
+        } else {
+            // row-major: rows SR .. 15 of the sub-tile lie past the resource's end
+            wrs[r] = buffer_rsrc(g.wq + (int64_t)base * K, nsub[r] < N ? (uint32_t)SR * K : 0u);
+        }
     }
-    const uint32_t lane_off = (uint32_t)(r16 * K + quarter * 32);
+    // packed: lanes of rows SR .. 15 read out of range (zeros)
+    const uint32_t lane_off = wpk ? (r16 < SR ? (uint32_t)(quarter * 256 + r16 * 16) : kOutOfRange)
+                                  : (uint32_t)(r16 * K + quarter * 32);
     // the lane's activation fragment in a staged block: [half 0][quarter][row]
     // (rows past R read an existing row, and their data is replaced by zeros)
     int lds_lo[MT];
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         const int k = kb * kGroup;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            slot[r] = load_w(wrs[r], lane_off, kb, k + quarter * 32, K, live);
+            slot[r] = load_w(wrs[r], lane_off, kb, k + quarter * 32, K, live, wpk);
             if constexpr (FMT == FMT_BLOCK) {
                 const int soff = __builtin_amdgcn_readfirstlane(
                     ((min(nsub[r], N - 1) / kGroup) * G + min(kb, G - 1)) * 4);
@@ -673,21 +690,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             }
         };
 
-        // Batches of PF blocks: compute a batch, then request the next one
-        // into the same slots (every slot on every pass, dead ones out of
-        // range).  One loop body for every batch, so the slots live in the
-        // same registers on every path.  Per-block work is a few MFMAs
-        // against the memory latency; the other waves of the compute unit
-        // keep the memory system busy while one computes.
-        for (int j = 0;; j += PF) {
+        // Rolling refill: as soon as slot p's block has been multiplied, the
+        // slot is requested again for the block PF places later, so PF - 1
+        // to PF blocks stay in flight the whole time (consuming a whole batch
+        // before requesting the next one would let the stream run dry once
+        // per batch).  In the steady-state loop every slot is requested on
+        // every pass (past the wave's blocks with out-of-range offsets), so
+        // each wait counts exactly PF - 1 younger blocks; the last partial
+        // batch is computed after the loop without new requests.  The loop
+        // body is unrolled by PF, so the slots live in fixed registers.
+        int j = 0;
+        for (; j + PF < nmine; j += PF) {
 #pragma unroll
-            for (int p = 0; p < PF; ++p)
-                if (j + p < nmine) compute(p, j + p);
-            if (j + PF >= nmine) break;
-#pragma unroll
-            for (int p = 0; p < PF; ++p)
+            for (int p = 0; p < PF; ++p) {
+                compute(p, j + p);
                 issue(wbuf[p], wsbuf[p], pb0 + kw + (j + PF + p) * kstep, j + PF + p < nmine);
+            }
         }
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+            if (j + p < nmine) compute(p, j + p);
     }
 
     if constexpr (FUSE && FMT != FMT_BLOCK) {

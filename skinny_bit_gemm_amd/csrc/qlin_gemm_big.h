@@ -160,7 +160,13 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
 
     // operand tiles through buffer resources (rows past M or N read zeros)
     const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(g.xq + (int64_t)m0 * K, (uint32_t)(rows_a * K));
-    const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(g.wq + (int64_t)n0 * K, (uint32_t)(rows_b * K));
+    // weights: row-major rows n0 .., or the packed 16-row groups n0 / 16 ..
+    // (2 KiB per group and K block; N is a multiple of 16)
+    const bool wpk = g.w_packed != 0;
+    const __amdgpu_buffer_rsrc_t brs =
+        wpk ? buffer_rsrc(g.wq + (int64_t)(n0 / kPackRows) * g.nkb * kPackBlock,
+                          (uint32_t)(rows_b / kPackRows * g.nkb * kPackBlock))
+            : buffer_rsrc(g.wq + (int64_t)n0 * K, (uint32_t)(rows_b * K));
     const __amdgpu_buffer_rsrc_t srs =
         buffer_rsrc(FMT == FMT_BLOCK ? (const void *)(g.xs + (int64_t)m0 * G) : (const void *)g.xs,
                     FMT == FMT_BLOCK ? (uint32_t)(rows_a * G * 4) : 0u);
@@ -171,6 +177,12 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     // position l % 8, which holds source chunk (l % 8) ^ (l / 8)
     const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
     const uint32_t lane_off = (uint32_t)(lrow * K + lchunk * 16);
+    // packed weights: source chunk c of row 8 hr + lrow of a 16-row group
+    // sits at (c & 1) KiB + 16 (16 (c >> 1) + 8 hr + lrow) in the group's
+    // block, so the same LDS layout fills from these lane offsets (one per
+    // half hr of the group; each request reads 8 whole 128-byte lines)
+    const uint32_t pk_off0 = (uint32_t)((lchunk & 1) * (kPackBlock / 2) + ((lchunk >> 1) * 16 + lrow) * 16);
+    const uint32_t pk_off1 = pk_off0 + 8 * 16;
     typedef __attribute__((address_space(3))) void *lds_ptr;
 
     // requests of block j of the range into LDS buffer `buf`
@@ -191,10 +203,19 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
 #pragma unroll
         for (int i = 0; i < T::REQ_B; ++i) {
             const int r0 = (wave * T::REQ_B + i) * 8;
-            const bool ok = kin && r0 + lrow < rows_b;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
-                                                     ok ? (uint32_t)(r0 * K) + lane_off : kOutOfRange,
-                                                     __builtin_amdgcn_readfirstlane(k0), 0, 0);
+            if (wpk) {
+                // (the packed layout holds zeros past K)
+                const bool ok = live && r0 + lrow < rows_b;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
+                    ok ? ((r0 >> 3) & 1 ? pk_off1 : pk_off0) : kOutOfRange,
+                    __builtin_amdgcn_readfirstlane(((r0 >> 4) * g.nkb + kb) * kPackBlock), 0, 0);
+            } else {
+                const bool ok = kin && r0 + lrow < rows_b;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
+                                                         ok ? (uint32_t)(r0 * K) + lane_off : kOutOfRange,
+                                                         __builtin_amdgcn_readfirstlane(k0), 0, 0);
+            }
         }
         if constexpr (FMT == FMT_BLOCK) {
             const uint32_t sbase = base + T::A_BYTES + T::B_BYTES;

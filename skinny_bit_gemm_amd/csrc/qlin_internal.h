@@ -12,6 +12,13 @@
 namespace qlin {
 
 constexpr int kGroup = 128;          // K block: one fp8 MFMA, one 1x128 scale group
+// packed weights (QLIN_PACKED_WEIGHTS): 16-row x 128-K blocks of 2 KiB
+constexpr int kPackRows = 16;
+constexpr int kPackBlock = kPackRows * kGroup;
+// bytes of one [N, K] weight matrix in the packed layout (N % 16 == 0)
+inline int64_t packed_weight_bytes(int N, int K) {
+    return (int64_t)(N / kPackRows) * ((K + kGroup - 1) / kGroup) * kPackBlock;
+}
 constexpr int kMaxWaves = 8;         // waves per workgroup
 constexpr int kLdsBudget = 78 * 1024; // bytes of LDS a GEMM workgroup may use (two fit a CU)
 constexpr int kMaxSplit = 64;
@@ -26,7 +33,7 @@ struct GemmLaunch {
     int64_t ldx;
     uint8_t *xq_out;     // ... and where the codes and scales it makes go
     float *xs_out;
-    const uint8_t *wq;
+    const uint8_t *wq;   // weight codes: [N][K] row-major, or packed (w_packed)
     const float *wsc;
     void *y;
     void *acc_ws;        // split-K: packed int64 sums [M][N] (zero between calls), or
@@ -48,6 +55,8 @@ struct GemmLaunch {
     // pairs of the groups that have rows, in group order (workgroups past
     // the last pair exit at once)
     int sub_rows;        // weight rows per 16-row sub-tile that are real (16, or 8)
+    int w_packed;        // weight codes in the packed layout (2 KiB blocks)
+    int64_t w_group_stride;   // bytes between the groups' weight matrices
     const int *group_off;
     int groups;
     int group_rows;      // rows per token tile of a grouped launch (<= tile_m)
@@ -84,6 +93,8 @@ hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, v
                             float *xs, hipStream_t s);
 hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, float *ws,
                                hipStream_t s);
+// [batch][N][K] row-major codes -> [batch][packed_weight_bytes(N, K)]
+hipError_t launch_pack_weight(int batch, int N, int K, const void *wq, void *out, hipStream_t s);
 // xc: register chunks per lane of the in-kernel quantization (0: unfused)
 hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, int xc, const GemmLaunch &g,
                        size_t lds_bytes, hipStream_t s);

@@ -150,7 +150,42 @@ __global__ __launch_bounds__(256) void quant_block_weight_kernel(const float *__
                   quant_code<FMT_BLOCK>(v.z, s), quant_code<FMT_BLOCK>(v.w, s));
     }
 }
+// ----------------------------------------------------------- weight packing
+
+// Row-major codes [batch][N][K] -> the packed layout: for 16-row group s,
+// K block kb, half h and lane l, the 16 bytes at byte
+// 1024 ((s * nkb + kb) * 2 + h) + 16 l hold row 16 s + l % 16, bytes
+// 128 kb + 32 (l / 16) + 16 h .. + 15 (zeros past K).  That is the GEMM
+// kernels' per-lane fragment of a 16-row x 128-K block, so a wave's weight
+// load reads 1 KiB of consecutive bytes.  One thread per 16-byte chunk:
+// coalesced stores, 16-byte gathers.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint8_t *__restrict__ w, int N, int K,
+                                                          int nkb, uint8_t *__restrict__ out) {
+    const int64_t per = (int64_t)(N / kPackRows) * nkb * (kPackBlock / 16);   // chunks per matrix
+    const uint8_t *src = w + (int64_t)blockIdx.y * N * K;
+    uint8_t *dst = out + (int64_t)blockIdx.y * per * 16;
+    for (int64_t c = blockIdx.x * (int64_t)256 + threadIdx.x; c < per; c += (int64_t)gridDim.x * 256) {
+        const int t = (int)(c & 127);
+        const int64_t blk = c >> 7;               // s * nkb + kb
+        const int kb = (int)(blk % nkb);
+        const int64_t row = (blk / nkb) * kPackRows + (t & 15);
+        const int k0 = kb * kGroup + 32 * ((t & 63) >> 4) + 16 * (t >> 6);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k0 < K) v = *reinterpret_cast<const uint4 *>(src + row * K + k0);
+        *reinterpret_cast<uint4 *>(dst + c * 16) = v;
+    }
+}
+
 // --------------------------------------------------------------- launchers
+
+hipError_t launch_pack_weight(int batch, int N, int K, const void *wq, void *out, hipStream_t s) {
+    const int nkb = (K + kGroup - 1) / kGroup;
+    const int64_t chunks = (int64_t)(N / kPackRows) * nkb * (kPackBlock / 16);
+    const int64_t blocks = (chunks + 255) / 256;
+    hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096), (unsigned)batch),
+                       dim3(256), 0, s, static_cast<const uint8_t *>(wq), N, K, nkb, static_cast<uint8_t *>(out));
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, void *xq,
                             float *xs, hipStream_t s) {

@@ -8,7 +8,8 @@ Benchmarking" (candidates are timed the way they run in production, under
 graph replay).  Here the search is exhaustive over a fixed candidate grid
 (schedule, tile, split factor, wave layout); each candidate is timed as a
 hipGraph of back-to-back layers (qlin_linear: quantize + GEMM) over distinct
-weight copies (>= 1 GiB in total, so the Infinity Cache cannot hold them).
+weight copies (>= 1 GiB in total, so the Infinity Cache cannot hold them),
+in the packed weight layout (--layout row-major for the other).
 A coarse pass over the schedule grid (each schedule with the quantization
 in its own kernel and fused into the GEMM), then the best few with each
 split-K reduction, then the best of those again with more replays.  With
@@ -121,13 +122,24 @@ def warm_graph(graph, stream, min_ms=20.0):
         q.qlin_graph_launch(graph, stream)
 
 
-class Bench:
-    """Device buffers for timing one (fmt, M, N, K) linear layer."""
+# the weight layout the table is tuned for: the packed layout of
+# qlin_pack_weight, which the decode path runs (row-major weights use the
+# same table)
+PACKED = True
 
-    def __init__(self, fmt, M, N, K, min_bytes=1 << 30):
+
+class Bench:
+    """Device buffers for timing one (fmt, M, N, K) linear layer.  The
+    weights are random codes (the timing does not depend on their values),
+    laid out as the packed layout's bytes unless `packed` is false."""
+
+    def __init__(self, fmt, M, N, K, min_bytes=1 << 30, packed=None):
         import torch
         self.torch = torch
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
+        packed = PACKED if packed is None else packed
+        self.call_fmt = fmt | (q.QLIN_PACKED_WEIGHTS if packed else 0)
+        wshape = (q.qlin_packed_weight_bytes(N, K),) if packed else (N, K)
         dev = "cuda"
         self.R = max(2, -(-min_bytes // (N * K)))
         g = torch.Generator(device=dev)
@@ -138,7 +150,7 @@ class Bench:
             if fmt != q.QLIN_W8A8_INT8:            # finite, modest fp8 codes
                 t = (t.view(torch.uint8) & 0xB7)
             return t
-        self.W = [codes((N, K)) for _ in range(self.R)]
+        self.W = [codes(wshape) for _ in range(self.R)]
         self.ws = torch.rand(q.scales_shape(fmt, N, K, True), device=dev, generator=g) * 1e-2
         self.x = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
         self.xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
@@ -149,7 +161,7 @@ class Bench:
         self.warm = False
 
     def _call(self, cfg, w, st):
-        q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, w, self.ws,
+        q.qlin_linear(self.call_fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, w, self.ws,
                       self.y, q.QLIN_OUT_BF16, cfg, self.work, stream=st)
 
     def time(self, cfg, replays=3):
@@ -283,7 +295,11 @@ def main(argv=None):
     ap.add_argument("--keep-margin", type=float, default=0.02,
                     help="with --merge: the fraction by which a new schedule must beat the existing entry")
     ap.add_argument("--report", default=None)
+    ap.add_argument("--layout", choices=("packed", "row-major"), default="packed",
+                    help="weight layout the candidates are timed on (default: packed)")
     args = ap.parse_args(argv)
+    global PACKED
+    PACKED = args.layout == "packed"
     Ms = [int(v) for v in args.m.split(",")]
     q.lib()
     entries, notes = {}, []

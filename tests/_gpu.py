@@ -58,6 +58,11 @@ def check_workspace(work: torch.Tensor, what: str = ""):
     assert int(work.count_nonzero()) == 0, f"{what}: workspace not left zero"
 
 
+def base_fmt(fmt: int) -> int:
+    """The number format of a format argument (without the weight-layout flag)."""
+    return fmt & ~q.QLIN_PACKED_WEIGHTS
+
+
 def to_dev_bf16(x_bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(DEV)
 
@@ -99,9 +104,19 @@ def gpu_quant_weight(fmt: int, w: np.ndarray):
     return wq, ws
 
 
+def gpu_pack(wq, N, K, batch=1):
+    """Row-major codes ([batch][N][K]) -> the packed layout, guarded."""
+    nb = q.qlin_packed_weight_bytes(N, K)
+    out = guarded((batch * nb,), torch.uint8, 0x5A)
+    q.qlin_pack_weight(batch, N, K, wq, out)
+    torch.cuda.synchronize()
+    check_guards(out, what=f"qlin_pack_weight batch={batch} N={N} K={K}")
+    return out
+
+
 def workspace_for(fmt, M, N, K, cfg):
     """A zeroed split-K workspace of the size the schedule needs, guarded."""
-    nbytes = q.qlin_workspace_bytes(fmt, M, N, K, cfg)
+    nbytes = q.qlin_workspace_bytes(base_fmt(fmt), M, N, K, cfg)
     return guarded((max(nbytes, 16),), torch.uint8, 0)
 
 
@@ -141,7 +156,7 @@ def gpu_linear(fmt, x_bits, wq, ws, N, cfg=None, out_type=q.QLIN_OUT_BF16, works
     padded[:, :K] = x_bits
     xd = to_dev_bf16(padded)
     xq = guarded((M, K), torch.uint8, 0x55)
-    xs = guarded(q.scales_shape(fmt, M, K, False), torch.float32, -1.0)
+    xs = guarded(q.scales_shape(base_fmt(fmt), M, K, False), torch.float32, -1.0)
     y = guarded((M, N), out_dtype(out_type), -1)
     if workspace is None:
         workspace = workspace_for(fmt, M, N, K, cfg)

@@ -107,6 +107,29 @@ def test_linear_scratch_checks_before_any_hip_call():
     assert call(M=0) == OK
 
 
+def test_pack_weight_checks_before_any_hip_call():
+    assert q.qlin_packed_weight_bytes(48, 1040) == 48 * 9 * 128      # blocks of 128 K, zero-padded
+    assert q.qlin_packed_weight_bytes(4096, 2048) == 4096 * 2048
+    def pack(batch=1, N=256, K=512, src=A, dst=A + (1 << 24)):
+        return q.qlin_pack_weight(batch, N, K, src, dst, stream=0, raise_on_error=False)
+    assert pack(N=100) == ESHAPE
+    assert pack(K=520) == ESHAPE
+    assert pack(batch=-1) == ESHAPE
+    assert pack(batch=70000) == ESHAPE
+    assert pack(src=None) == EINVAL
+    assert pack(dst=A + 8) == EALIGN
+    assert pack(batch=0) == OK                                       # nothing to do
+    # the layout flag on the format argument: accepted by the GEMM calls and
+    # the schedule queries, rejected by the quantizers
+    flag = q.QLIN_PACKED_WEIGHTS
+    assert q.qlin_validate_config(FP8 | flag, 4, 256, 512, q.make_config()) == OK
+    assert q.qlin_workspace_bytes(I8 | flag, 4, 256, 512, q.make_config(split_k=2)) == \
+        q.qlin_workspace_bytes(I8, 4, 256, 512, q.make_config(split_k=2))
+    assert gemm(fmt=BLK | flag, K=640 + 16) == ESHAPE
+    assert gemm(fmt=7 | flag) == EINVAL
+    assert q.qlin_quantize_act(FP8 | flag, 4, 512, A, 512, A, A, stream=0, raise_on_error=False) == EINVAL
+
+
 def test_gemm_rejects_bad_configs():
     bad = [q.make_config(swap_ab=2), q.make_config(split_k=0), q.make_config(split_k=65),
            q.make_config(tile_m=8), q.make_config(waves=0, k_waves=1),

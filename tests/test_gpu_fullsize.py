@@ -3,7 +3,8 @@ benchmark times (qlin_linear with the selection table's schedule), and the
 crossover sweep above 32 tokens with every schedule forced.
 
 The layers of the three model workloads are compared in full at every token
-count: codes, scales, the whole bf16 output against oracle.gemm (and, for
+count, with the weights packed (the benchmark's layout) and row-major:
+codes, scales, the whole bf16 output against oracle.gemm (and, for
 W8A8_INT8, the whole int32 accumulator array bit for bit).  The crossover
 sweep compares whole outputs at 64 tokens and a sample of positions the
 oracle computes one by one (corners, tile edges and random positions) above;
@@ -20,7 +21,9 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import DEV, as_u8, gpu_gemm, gpu_linear, gpu_quant_weight, to_dev, y_to_numpy  # noqa: E402
+from _gpu import DEV, as_u8, gpu_gemm, gpu_linear, gpu_pack, gpu_quant_weight, to_dev, y_to_numpy  # noqa: E402
+
+PACKED_W = q.QLIN_PACKED_WEIGHTS
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -90,18 +93,21 @@ def test_full_size_layers(fmt, layer):
     del w
     assert np.array_equal(as_u8(wq), qw), "weight codes differ"
     assert np.array_equal(ws.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    wp = gpu_pack(wq, N, K)          # the layout the benchmark runs
     for M in (1, 2, 4, 7, 16, 24, 32):   # one token count in each tuned bucket
         x = wl.activations(fmt, N, K, M)
         qa, sa = oracle.quant_act(fmt, x)
         print(f"[full]   M={M} schedule={q.qlin_select_variant(fmt, M, N, K)}", flush=True)
-        xq, xs, y = gpu_linear(fmt, x, wq, ws, N, None)       # the table's schedule
-        assert np.array_equal(as_u8(xq), qa), f"M={M}: activation codes differ"
-        assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa.view(np.uint32))
-        acc_y = None
-        if fmt == wl.W8A8_INT8:
-            _, _, yi = gpu_linear(fmt, x, wq, ws, N, None, out_type=q.QLIN_OUT_I32_ACC)
-            acc_y = yi.cpu().numpy()
-        check_whole(fmt, y, qa, sa, qw, sw, acc_y, what=f"M={M}")
+        expected = oracle_whole(fmt, qa, sa, qw, sw)
+        for layout, (f, wt) in {"packed": (fmt | PACKED_W, wp), "row-major": (fmt, wq)}.items():
+            xq, xs, y = gpu_linear(f, x, wt, ws, N, None)       # the table's schedule
+            assert np.array_equal(as_u8(xq), qa), f"M={M} {layout}: activation codes differ"
+            assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa.view(np.uint32))
+            acc_y = None
+            if fmt == wl.W8A8_INT8:
+                _, _, yi = gpu_linear(f, x, wt, ws, N, None, out_type=q.QLIN_OUT_I32_ACC)
+                acc_y = yi.cpu().numpy()
+            check_whole(fmt, y, qa, sa, qw, sw, acc_y, what=f"M={M} {layout}", expected=expected)
 
 
 def forced(fmt, M, N, K):
@@ -132,6 +138,7 @@ def test_crossover_sweep_variants(fmt, layer):
     qw, sw = oracle.quant_weight(fmt, w)
     wq, ws = gpu_quant_weight(fmt, w)
     del w
+    wp = gpu_pack(wq, N, K)
     for M in (64, 128, 256, 512):
         x = wl.activations(fmt, N, K, M)
         qa, sa = oracle.quant_act(fmt, x)
@@ -148,4 +155,6 @@ def test_crossover_sweep_variants(fmt, layer):
                 check_whole(fmt, y, qa, sa, qw, sw, acc_y, what=f"M={M} {name}", expected=expected)
             else:
                 check_sampled(fmt, y, qa, sa, qw, sw, M, N, acc_y, seed=M + len(name))
+            # packed weights: bit-identical to the row-major result
+            assert torch.equal(gpu_gemm(fmt | PACKED_W, xq, xs, wp, ws, M, N, K, c), y), f"M={M} {name} packed"
         del xq, xs

@@ -11,7 +11,7 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import (DEV, as_u8, check_guards, check_workspace, gpu_quant_weight, guarded,  # noqa: E402
+from _gpu import (DEV, as_u8, check_guards, check_workspace, gpu_pack, gpu_quant_weight, guarded,  # noqa: E402
                   to_dev_bf16, workspace_for)
 
 FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
@@ -26,12 +26,16 @@ def _gpu_ready():
 
 
 class Layer:
-    def __init__(self, fmt, M, N, K, seed, cfg=None):
+    def __init__(self, fmt, M, N, K, seed, cfg=None, packed=False):
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
         self.x_np = wl.activations(fmt, N, K, M)
         self.w_np = wl.random_weights(N, K, seed)
         self.x = to_dev_bf16(self.x_np)
         self.wq, self.ws = gpu_quant_weight(fmt, self.w_np)
+        self.call_fmt = fmt
+        if packed:   # weights in the packed layout
+            self.wq = gpu_pack(self.wq, N, K)
+            self.call_fmt = fmt | q.QLIN_PACKED_WEIGHTS
         self.xq = guarded((M, K), torch.uint8)
         self.xs = guarded(q.scales_shape(fmt, M, K, False), torch.float32)
         self.y = guarded((M, N), torch.int16)
@@ -45,7 +49,7 @@ class Layer:
         check_workspace(self.work, what=what)
 
     def run(self, stream):
-        q.qlin_linear(self.fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, self.wq,
+        q.qlin_linear(self.call_fmt, self.M, self.N, self.K, self.x, self.K, self.xq, self.xs, self.wq,
                       self.ws, self.y, q.QLIN_OUT_BF16, self.cfg, self.work, stream=stream)
 
 
@@ -65,7 +69,8 @@ def test_graph_replays_equal_eager(fmt):
             q.make_config(1, 4, 16, 32, 4, 2, 0, 1),               # fused, slice reduction
             q.make_config(0, 3, 32, 64, 4, 4, 0, 0),               # unfused, M tile 32
             q.make_config(1, 8, 16, 64, 4, 4, 1 if fmt != wl.BLOCK_FP8 else 0, 0)]
-    layers = [Layer(fmt, M, 512, 2048, 10 + i, c) for i, (M, c) in enumerate(zip((1, 5, 24, 16), cfgs))]
+    layers = [Layer(fmt, M, 512, 2048, 10 + i, c, packed=i % 2 == 1)
+              for i, (M, c) in enumerate(zip((1, 5, 24, 16), cfgs))]
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for l in layers:

@@ -16,8 +16,10 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import (DEV, as_u8, check_guards, check_workspace, gpu_quant_act, guarded, out_dtype,  # noqa: E402
-                  to_dev, y_to_numpy)
+from _gpu import (DEV, as_u8, check_guards, check_workspace, gpu_pack, gpu_quant_act, guarded,  # noqa: E402
+                  out_dtype, to_dev, y_to_numpy)
+
+PACKED_W = q.QLIN_PACKED_WEIGHTS
 
 FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
 FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
@@ -87,10 +89,15 @@ def check_case(fmt, E, N, K, T, topk, seed, c, max_rows=None):
     ref = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw)
     ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
     assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
+    # the experts' weights packed (one matrix after another): bit-identical
+    wpd = gpu_pack(wqd, N, K, batch=E)
+    assert torch.equal(run(fmt | PACKED_W, offsets, xq, xs, wpd, wsd, E, N, K, max_rows, c), y), "packed weights"
     if fmt == wl.W8A8_INT8:
         _, acc = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw, want_acc=True)
         yi = run(fmt, offsets, xq, xs, wqd, wsd, E, N, K, max_rows, c, q.QLIN_OUT_I32_ACC)
         assert np.array_equal(yi.cpu().numpy(), acc), "int32 accumulators differ"
+        yip = run(fmt | PACKED_W, offsets, xq, xs, wpd, wsd, E, N, K, max_rows, c, q.QLIN_OUT_I32_ACC)
+        assert np.array_equal(yip.cpu().numpy(), acc), "packed weights: int32 accumulators differ"
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
@@ -185,7 +192,8 @@ def test_grouped_moe_layer_shape(fmt, layer, T):
         w = np.random.default_rng(9000 + e).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
         qw[e], sw[e] = oracle.quant_weight(fmt, w)
     print(f"[grouped-moe] fmt={fmt} {layer.name} T={T} active={len(active)}", flush=True)
-    y = run(fmt, offsets, xq, xs, to_dev(qw), to_dev(sw), E, N, K, T, None)
+    wpd = gpu_pack(to_dev(qw), N, K, batch=E)
+    y = run(fmt | PACKED_W, offsets, xq, xs, wpd, to_dev(sw), E, N, K, T, None)
     ref = oracle.grouped_gemm(fmt, offsets, qa, sa, qw, sw)
     ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
     assert ok and len(active) > 16, (worst, len(active))

@@ -2,7 +2,9 @@
 
 Bars: quantized codes and fp32 scales bit-exact; int8 int32 accumulators
 bit-exact for every schedule; bf16 outputs within
-|y - ref| <= 1e-2 |ref| + 1e-3 max|ref|.
+|y - ref| <= 1e-2 |ref| + 1e-3 max|ref|.  Every schedule runs on row-major
+weights and on the same weights packed by qlin_pack_weight, whose outputs
+must be bit-identical.
 """
 import numpy as np
 import pytest
@@ -14,8 +16,10 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import (as_u8, gpu_gemm, gpu_linear, gpu_quant_act, gpu_quant_weight,  # noqa: E402
+from _gpu import (as_u8, gpu_gemm, gpu_linear, gpu_pack, gpu_quant_act, gpu_quant_weight,  # noqa: E402
                   workspace_for, y_to_numpy)
+
+PACKED_W = q.QLIN_PACKED_WEIGHTS   # weight-layout flag of the format argument
 
 FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
 FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
@@ -90,13 +94,20 @@ def check_linear(fmt, M, N, K, x, w, sched, tag=""):
     assert np.array_equal(as_u8(xq), qa_o), "activation codes differ"
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa_o.view(np.uint32)), "activation scales differ"
     c = SCHEDULES[sched] if isinstance(sched, str) else sched
-    y = y_to_numpy(gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c))
+    yt = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c)
+    y = y_to_numpy(yt)
     ok, worst = oracle.tolerance_ok(y, ref)
     assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
+    # the same schedule on packed weights: the same operands reach the
+    # matrix cores, so the output is bit-identical
+    wp = gpu_pack(wq, N, K)
+    assert torch.equal(gpu_gemm(fmt | PACKED_W, xq, xs, wp, ws, M, N, K, c), yt), "packed weights: outputs differ"
     if fmt == wl.W8A8_INT8:
         _, acc = oracle.gemm(fmt, qa_o, sa_o, qw_o, sw_o, want_acc=True)
         yi = gpu_gemm(fmt, xq, xs, wq, ws, M, N, K, c, out_type=q.QLIN_OUT_I32_ACC).cpu().numpy()
         assert np.array_equal(yi, acc), "int32 accumulators differ"
+        yp = gpu_gemm(fmt | PACKED_W, xq, xs, wp, ws, M, N, K, c, out_type=q.QLIN_OUT_I32_ACC).cpu().numpy()
+        assert np.array_equal(yp, acc), "packed weights: int32 accumulators differ"
     return y, ref
 
 
@@ -137,10 +148,16 @@ def check_layer(fmt, M, N, K, x, w, c, ldx=None):
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa_o.view(np.uint32)), "activation scales differ"
     ok, worst = oracle.tolerance_ok(y_to_numpy(y), ref)
     assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
+    wp = gpu_pack(wq, N, K)
+    xqp, xsp, yp = gpu_linear(fmt | PACKED_W, x, wp, ws, N, c, ldx=ldx)
+    assert torch.equal(xqp, xq) and torch.equal(xsp, xs), "packed weights: codes or scales differ"
+    assert torch.equal(yp, y), "packed weights: outputs differ"
     if fmt == wl.W8A8_INT8:
         _, acc = oracle.gemm(fmt, qa_o, sa_o, qw_o, sw_o, want_acc=True)
         _, _, yi = gpu_linear(fmt, x, wq, ws, N, c, out_type=q.QLIN_OUT_I32_ACC, ldx=ldx)
         assert np.array_equal(yi.cpu().numpy(), acc), "int32 accumulators differ"
+        _, _, yip = gpu_linear(fmt | PACKED_W, x, wp, ws, N, c, out_type=q.QLIN_OUT_I32_ACC, ldx=ldx)
+        assert np.array_equal(yip.cpu().numpy(), acc), "packed weights: int32 accumulators differ"
 
 
 # In-kernel quantization holds the tile's activation rows (8-value chunks,

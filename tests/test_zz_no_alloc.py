@@ -15,8 +15,8 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-from _gpu import (as_u8, check_guards, gpu_linear, gpu_quant_weight, guarded, out_dtype,  # noqa: E402
-                  to_dev_bf16, y_to_numpy)
+from _gpu import (as_u8, base_fmt, check_guards, gpu_linear, gpu_pack, gpu_quant_weight, guarded,  # noqa: E402
+                  out_dtype, to_dev_bf16, y_to_numpy)
 
 FMTS = [wl.FP8_DYNAMIC, wl.W8A8_INT8, wl.BLOCK_FP8]
 FMT_IDS = ["fp8_dynamic", "w8a8_int8", "block_fp8"]
@@ -34,7 +34,7 @@ def scratch_linear(fmt, x_bits, wq, ws, N, cfg, out_type=q.QLIN_OUT_BF16):
     M, K = x_bits.shape
     xd = to_dev_bf16(x_bits)
     xq = guarded((M, K), torch.uint8, 0x55)
-    xs = guarded(q.scales_shape(fmt, M, K, False), torch.float32, -1.0)
+    xs = guarded(q.scales_shape(base_fmt(fmt), M, K, False), torch.float32, -1.0)
     y = guarded((M, N), out_dtype(out_type), -1)
     q.qlin_linear_scratch(fmt, M, N, K, xd, K, xq, xs, wq, ws, y, out_type, cfg)
     torch.cuda.synchronize()
@@ -67,6 +67,9 @@ def check_pair(fmt, M, N, K, c, seed):
     assert torch.equal(y0, y1), "outputs differ from qlin_linear's"
     ok, worst = oracle.tolerance_ok(y_to_numpy(y1), ref)
     assert ok, f"bf16 output outside tolerance (worst ratio {worst:.3g})"
+    # and with the weights packed
+    _, _, y2 = scratch_linear(fmt | q.QLIN_PACKED_WEIGHTS, x, gpu_pack(wq, N, K), ws, N, c)
+    assert torch.equal(y2, y1), "packed weights: outputs differ"
     if fmt == wl.W8A8_INT8:
         _, acc = oracle.gemm(fmt, qa, sa, qw, sw, want_acc=True)
         _, _, yi = scratch_linear(fmt, x, wq, ws, N, c, q.QLIN_OUT_I32_ACC)
