@@ -177,12 +177,11 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     // position l % 8, which holds source chunk (l % 8) ^ (l / 8)
     const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
     const uint32_t lane_off = (uint32_t)(lrow * K + lchunk * 16);
-    // packed weights: source chunk c of row 8 hr + lrow of a 16-row group
-    // sits at (c & 1) KiB + 16 (16 (c >> 1) + 8 hr + lrow) in the group's
-    // block, so the same LDS layout fills from these lane offsets (one per
-    // half hr of the group; each request reads 8 whole 128-byte lines)
-    const uint32_t pk_off0 = (uint32_t)((lchunk & 1) * (kPackBlock / 2) + ((lchunk >> 1) * 16 + lrow) * 16);
-    const uint32_t pk_off1 = pk_off0 + 8 * 16;
+    // Packed weights keep their own order in LDS: the tile's 16-row groups,
+    // 2 KiB apart (as 16 row-major rows would be), each the packed block
+    // itself, so one request copies 1 KiB of consecutive bytes (half a
+    // group) to consecutive LDS, and a lane's fragment halves are at 16 lane
+    // and 16 lane + 1 KiB of its group.
     typedef __attribute__((address_space(3))) void *lds_ptr;
 
     // requests of block j of the range into LDS buffer `buf`
@@ -204,12 +203,15 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
         for (int i = 0; i < T::REQ_B; ++i) {
             const int r0 = (wave * T::REQ_B + i) * 8;
             if (wpk) {
-                // (the packed layout holds zeros past K)
-                const bool ok = live && r0 + lrow < rows_b;
+                // request j = r0 / 8 is half j % 2 of group j / 2 (the packed
+                // layout holds zeros past K)
+                const int j = r0 >> 3;
+                const bool ok = live && (j >> 1) * kPackRows < rows_b;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
-                    ok ? ((r0 >> 3) & 1 ? pk_off1 : pk_off0) : kOutOfRange,
-                    __builtin_amdgcn_readfirstlane(((r0 >> 4) * g.nkb + kb) * kPackBlock), 0, 0);
+                    ok ? (uint32_t)lane * 16 : kOutOfRange,
+                    __builtin_amdgcn_readfirstlane(((j >> 1) * g.nkb + kb) * kPackBlock + (j & 1) * (kPackBlock / 2)),
+                    0, 0);
             } else {
                 const bool ok = kin && r0 + lrow < rows_b;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
@@ -241,13 +243,19 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     const int a_row = wm * T::WM + r16, b_row = wn * 64 + r16;
     const int sw = r16 & 7;   // row & 7 (group bases are multiples of 16)
     const uint32_t c_lo = ((2 * quarter) ^ sw) * 16, c_hi = ((2 * quarter + 1) ^ sw) * 16;
+    // the lane's weight fragment halves within the B tile: row-major (the
+    // swizzled rows), or packed (the wave's first 16-row group, 16 lane and
+    // 16 lane + 1 KiB)
+    const uint32_t b_lo = wpk ? (uint32_t)((wn * 64 / kPackRows) * kPackBlock + lane * 16)
+                              : (uint32_t)(b_row * kGroup) + c_lo;
+    const uint32_t b_hi = wpk ? b_lo + kPackBlock / 2 : (uint32_t)(b_row * kGroup) + c_hi;
     // one block from the buffer at b0: the channel fragments and the first
     // token fragment, its products, then the requests of a later block
     // (`after`, so that they leave while the matrix core works), then the
     // other token fragments and their products
     auto compute = [&](uint32_t b0, auto after) {
         const uint32_t al = b0 + a_row * kGroup + c_lo, ah = b0 + a_row * kGroup + c_hi;
-        const uint32_t bl = b0 + T::A_BYTES + b_row * kGroup + c_lo, bh = b0 + T::A_BYTES + b_row * kGroup + c_hi;
+        const uint32_t bl = b0 + T::A_BYTES + b_lo, bh = b0 + T::A_BYTES + b_hi;
         v4i a[2], b[T::FN][2];
         v8i bf[T::FN];
         if constexpr (FMT == FMT_BLOCK) {

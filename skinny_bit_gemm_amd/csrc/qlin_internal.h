@@ -21,6 +21,10 @@ inline int64_t packed_weight_bytes(int N, int K) {
 }
 constexpr int kMaxWaves = 8;         // waves per workgroup
 constexpr int kLdsBudget = 78 * 1024; // bytes of LDS a GEMM workgroup may use (two fit a CU)
+// ... and when the launch has no more workgroups than the GPU has compute
+// units (each gets a CU of its own, with 160 KiB of LDS)
+constexpr int kLdsBudgetOnePerCU = 150 * 1024;
+constexpr int kComputeUnits = 256;
 constexpr int kMaxSplit = 64;
 // size of the static split-K workspace of qlin_linear_scratch (per GPU)
 constexpr size_t kScratchBytes = QLIN_SCRATCH_BYTES;
@@ -78,8 +82,10 @@ struct Plan {
 
 // Fills *plan; returns QLIN_OK or the reason the schedule is invalid.
 // `fused`: planned for qlin_linear (cfg.fuse_quant applies) or qlin_gemm.
+// `grouped`: for a grouped launch, whose grid is not the plan's own (its
+// workgroups keep the smaller LDS budget).
 qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &cfg, bool fused,
-                      Plan *plan);
+                      Plan *plan, bool grouped = false);
 
 // Host-side selection table (qlin_table.cpp).
 qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out, bool *found);

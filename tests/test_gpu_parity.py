@@ -202,8 +202,9 @@ def test_linear_fused_few_waves(fmt):
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 def test_linear_fused_packed_stride_and_phases(fmt):
     """Fused quantization with packed reduction and a row stride larger than
-    K; unfused with LDS phases (16 rows x 8192 codes exceed one stage), where
-    the fused form is rejected."""
+    K; unfused with 16 rows x 8192 codes (one 128 KiB stage on this small
+    grid), where the fused form is rejected (16 rows of 1024 chunks do not
+    fit 8 register chunks per thread)."""
     N, K = 256, 8192
     w = wl.random_weights(N, K, 61)
     red = 1 if fmt != wl.BLOCK_FP8 else 0
@@ -219,14 +220,18 @@ def test_linear_fused_packed_stride_and_phases(fmt):
 def test_staging_phases_ragged(fmt):
     """Activation staging over several LDS phases with a shorter last phase,
     ragged token rows (29 of a 32-row tile) and, for the per-token formats,
-    a partial last K block: 29 rows x 65 K blocks take phases of 21, 21, 21
-    and 2 blocks, each row copied in requests of up to 8 blocks."""
-    M, N = 29, 256
+    a partial last K block (65 K blocks, each row copied in requests of up
+    to 8 blocks).  A launch of at most one workgroup per compute unit stages
+    up to 150 KiB at a time (29 rows x 65 blocks take 2 phases); a larger
+    grid (N = 4352 in 16-row tiles: 272 workgroups) 78 KiB (4 phases)."""
+    M = 29
     K = 8320 if fmt == wl.BLOCK_FP8 else 8240
-    x = wl.activations(fmt, N, K, M) if K % 128 == 0 else wl.random_bf16((M, K), 17)
-    w = wl.random_weights(N, K, 18)
-    for c in (cfg(1, 1, 32, 32, 4, 2), cfg(0, 2, 32, 64, 8, 2)):
-        check_layer(fmt, M, N, K, x, w, c)
+    for N, cs in ((256, (cfg(1, 1, 32, 32, 4, 2), cfg(0, 2, 32, 64, 8, 2))),
+                  (4352, (cfg(1, 1, 32, 16, 4, 4), cfg(0, 1, 32, 16, 2, 1)))):
+        x = wl.activations(fmt, N, K, M) if K % 128 == 0 else wl.random_bf16((M, K), 17)
+        w = wl.random_weights(N, K, 18)
+        for c in cs:
+            check_layer(fmt, M, N, K, x, w, c)
 
 
 @pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
