@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--also", default=DEFAULT_ALSO,
                     help="other workloads whose step and GEMM launches are timed the same way and "
                          "reported under other_workloads ('' for none)")
+    ap.add_argument("--quant", default=None,
+                    help="instead of the step: time every launch shape of the activation quantize kernels "
+                         "on the three model workloads' (M, K) and write it (JSON) here")
     ap.add_argument("--floors", default=None,
                     help="instead of the step: time the graph-replayed streaming read of every layer "
                          "size of the three model workloads and write it (JSON) here")
@@ -111,7 +114,8 @@ class Linear:
 
     @property
     def fused(self):
-        return bool(self.cfg.fuse_quant)
+        import skinny_bit_gemm_amd as q
+        return self.cfg.act_path == q.QLIN_ACT_FUSED
 
     def kernel(self, stream, wq=None):
         """The step's GEMM kernel of this linear, as the step runs it: the
@@ -631,6 +635,52 @@ def floors_bench(path):
     return {"mode": "floors", "sizes": len(rows), "file": path, "read_ceiling_GBps": round(ceiling, 1)}
 
 
+QUANT_THREADS = {0: (64, 128, 256, 512), 1: (64, 128, 256, 512), 2: (64, 256)}
+
+
+def quant_bench(path):
+    """The activation quantize kernels alone: every launch shape
+    (qlin_quantize_act_cfg) at every (token count, K) of the three model
+    workloads, each timed as a hipGraph of 64 launches (what a decode step
+    pays per unfused layer, launch included)."""
+    import torch
+    import skinny_bit_gemm_amd as q
+    from skinny_bit_gemm_amd.tune import warm_graph
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    st = torch.cuda.Stream()
+    rows = []
+    with torch.cuda.stream(st):
+        for name in ("fp8_dynamic_hidden2048", "w8a8_int8_hidden4096", "block_fp8_hidden5120"):
+            fmt, layers, Ms = wl.WORKLOADS[name]
+            for K in sorted({L.K for L in layers}):
+                for M in Ms:
+                    x = torch.from_numpy(wl.activations(fmt, 128, K, M).view("int16")).to(dev)
+                    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                    xs = torch.empty(q.scales_shape(fmt, M, K, False), dtype=torch.float32, device=dev)
+                    point = {"format": wl.FORMAT_NAMES[fmt], "M": M, "K": K, "us": {}}
+                    for t in QUANT_THREADS[fmt] + (0,):
+                        run = lambda: [q.qlin_quantize_act_cfg(fmt, M, K, x, K, xq, xs, t, stream=st)
+                                       for _ in range(64)]
+                        run()
+                        g = capture(st, run)
+                        warm_graph(g, st)
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(st)
+                        for _ in range(5):
+                            q.qlin_graph_launch(g, st)
+                        e1.record(st)
+                        torch.cuda.synchronize()
+                        q.qlin_graph_destroy(g)
+                        point["us"][str(t) if t else "rule"] = round(e0.elapsed_time(e1) * 1e3 / (5 * 64), 3)
+                    rows.append(point)
+                    print(f"[quant] {point}", file=sys.stderr, flush=True)
+    with open(path, "w") as f:
+        json.dump(rows, f, indent=1)
+    return {"mode": "quant", "points": len(rows), "file": path}
+
+
 def workload_summary(r):
     """Step and GEMM-launch numbers of one timed workload."""
     value = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
@@ -677,6 +727,9 @@ def main():
     q.lib()
     if args.floors:
         print(json.dumps(floors_bench(args.floors)), flush=True)
+        return
+    if args.quant:
+        print(json.dumps(quant_bench(args.quant)), flush=True)
         return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)

@@ -82,6 +82,11 @@ typedef enum {
     QLIN_ERR_HIP = 7          /* a HIP runtime call failed                   */
 } qlin_status;
 
+/* act_path values of qlin_config */
+#define QLIN_ACT_STAGED 0
+#define QLIN_ACT_FUSED 1
+#define QLIN_ACT_DIRECT 2
+
 /* One schedule of the contraction (section "Kernel Implementation": the
  * split_k and swap_ab tunables, plus the tile shape and how the pieces are
  * put back together).
@@ -94,7 +99,7 @@ typedef enum {
  *   tile_m     tokens per tile: 16 or 32 (the skinny kernel), or 64 or 128
  *              (the large-M kernel for token counts past the skinny range:
  *              it needs tile_n 128, waves 4, k_waves 1, swap_ab 0,
- *              reduce 0, fuse_quant 0).
+ *              reduce 0, act_path 0).
  *   tile_n     output channels per workgroup, <= 256: 1, 2 or 4 times
  *              16 x (waves / k_waves) (16-row weight sub-tiles, the matrix
  *              core's), or exactly 8 x (waves / k_waves) (8-row sub-tiles:
@@ -111,11 +116,22 @@ typedef enum {
  *              1 = exact packed 64-bit integer atomics (W8A8_INT8, and
  *              FP8_DYNAMIC with K <= 40960).  Both give results that do
  *              not depend on the order partitions finish in.
- *   fuse_quant qlin_linear only: 1 = each GEMM workgroup quantizes the
- *              activations it needs itself (one kernel instead of two;
- *              needs tile_m 16, the K range in one LDS stage and the tile's
- *              activation rows within 8 register chunks of 8 values per
- *              thread); ignored by qlin_gemm.                               */
+ *   act_path   how the GEMM workgroups get their activation codes:
+ *              QLIN_ACT_STAGED (0): quantized beforehand (qlin_linear
+ *                enqueues qlin_quantize_act first) and copied into the
+ *                LDS in K-block stages that all of the workgroup's waves
+ *                read;
+ *              QLIN_ACT_FUSED (1), qlin_linear only (qlin_gemm takes it
+ *                as 0): each workgroup quantizes the rows it needs itself
+ *                (one kernel instead of two; needs tile_m 16, the K range
+ *                in one LDS stage and the tile's activation rows within 8
+ *                register chunks of 8 values per thread);
+ *              QLIN_ACT_DIRECT (2): quantized beforehand, and each wave
+ *                loads the fragments of its own K blocks from memory with
+ *                the weight blocks they multiply (no LDS stage and no
+ *                prologue that waits for one); the skinny kernel only
+ *                (tile_m 16 or 32), and for QLIN_BLOCK_FP8 only with
+ *                swap_ab 1.                                                  */
 typedef struct {
     int32_t swap_ab;
     int32_t split_k;
@@ -124,7 +140,7 @@ typedef struct {
     int32_t waves;
     int32_t k_waves;
     int32_t reduce;
-    int32_t fuse_quant;
+    int32_t act_path;
 } qlin_config;
 
 /* Activation quantization (per token, or per token and 1x128 group for
@@ -135,6 +151,16 @@ typedef struct {
  * M may be 0 (nothing is enqueued). */
 qlin_status qlin_quantize_act(qlin_format fmt, int M, int K, const void *x, int64_t ldx,
                               void *xq, float *x_scales, void *stream);
+
+/* qlin_quantize_act with the kernel's launch shape chosen by the caller (the
+ * small config set the built-in rule picks from, exposed for measuring it):
+ *   threads  per-token formats: threads per token row, 64, 128, 256 or 512
+ *            (one wave per row needs no exchange between waves);
+ *            QLIN_BLOCK_FP8: threads per workgroup, 64 or 256 (16 per group);
+ *            0: the built-in rule (what qlin_quantize_act does).
+ * Codes and scales do not depend on it.  Other values: QLIN_ERR_INVALID_ARG. */
+qlin_status qlin_quantize_act_cfg(qlin_format fmt, int M, int K, const void *x, int64_t ldx,
+                                  void *xq, float *x_scales, int threads, void *stream);
 
 /* Weight quantization (offline preparation; same rules, one scale per output
  * channel, or per 128x128 block for QLIN_BLOCK_FP8).
@@ -181,8 +207,9 @@ qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq,
                       size_t ws_bytes, void *stream);
 
 /* The whole layer: quantize x (as qlin_quantize_act; xq and x_scales are
- * written) and compute y (as qlin_gemm).  With cfg->fuse_quant (or the
- * table's choice when cfg is NULL) this is one kernel launch, else two.
+ * written) and compute y (as qlin_gemm).  With act_path QLIN_ACT_FUSED in
+ * cfg (or in the table's choice when cfg is NULL) this is one kernel
+ * launch, else two.
  * Arguments, layouts and errors are those of the two calls; x must not
  * alias xq, x_scales or y. */
 qlin_status qlin_linear(qlin_format fmt, int M, int N, int K, const void *x, int64_t ldx, void *xq,
@@ -258,7 +285,8 @@ qlin_status qlin_validate_config(qlin_format fmt, int M, int N, int K, const qli
  *                  [groups][N/128][K/128] for QLIN_BLOCK_FP8) scales
  *   y              [total_rows, N]
  *   cfg            NULL: qlin_grouped_select_variant's rule; otherwise
- *                  forced (tile_m 16 or 32, fuse_quant 0)
+ *                  forced (tile_m 16 or 32, act_path QLIN_ACT_STAGED or
+ *                  QLIN_ACT_DIRECT)
  *   workspace      as qlin_gemm, qlin_grouped_workspace_bytes(...) bytes
  * The grid covers ceil(total_rows / tile rows) + min(groups, total_rows)
  * token tiles, a bound on the tiles of any routing; workgroups past the

@@ -32,7 +32,7 @@ EXPORTS = (
     "qlin_table_entries", "qlin_graph_begin", "qlin_graph_end", "qlin_graph_launch",
     "qlin_graph_destroy", "qlin_status_str", "qlin_abi_version", "qlin_last_hip_error",
     "qlin_grouped_gemm", "qlin_grouped_select_variant", "qlin_grouped_workspace_bytes",
-    "qlin_linear_scratch", "qlin_packed_weight_bytes", "qlin_pack_weight",
+    "qlin_linear_scratch", "qlin_packed_weight_bytes", "qlin_pack_weight", "qlin_quantize_act_cfg",
 )
 # format flag: the weight codes are in the packed layout of qlin_pack_weight
 QLIN_PACKED_WEIGHTS = 0x100
@@ -50,11 +50,16 @@ class QlinError(RuntimeError):
         super().__init__(f"{what}: {name}{extra}")
 
 
+# qlin_config.act_path: activation codes staged in the LDS, quantized inside
+# the GEMM, or loaded by each wave directly
+QLIN_ACT_STAGED, QLIN_ACT_FUSED, QLIN_ACT_DIRECT = 0, 1, 2
+
+
 class qlin_config(ctypes.Structure):
     _fields_ = [("swap_ab", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("k_waves", ctypes.c_int32),
-                ("reduce", ctypes.c_int32), ("fuse_quant", ctypes.c_int32)]
+                ("reduce", ctypes.c_int32), ("act_path", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: int(getattr(self, f)) for f, _ in self._fields_}
@@ -64,8 +69,8 @@ class qlin_config(ctypes.Structure):
 
 
 def make_config(swap_ab=0, split_k=1, tile_m=16, tile_n=32, waves=4, k_waves=4, reduce=0,
-                fuse_quant=0) -> qlin_config:
-    return qlin_config(swap_ab, split_k, tile_m, tile_n, waves, k_waves, reduce, fuse_quant)
+                act_path=0) -> qlin_config:
+    return qlin_config(swap_ab, split_k, tile_m, tile_n, waves, k_waves, reduce, act_path)
 
 
 _lib = None
@@ -90,6 +95,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.qlin_quantize_act.argtypes = [_I, _I, _I, _P, _I64, _P, _P, _P]
         L.qlin_quantize_weight.argtypes = [_I, _I, _I, _P, _P, _P, _P]
+        L.qlin_quantize_act_cfg.argtypes = [_I, _I, _I, _P, _I64, _P, _P, _I, _P]
         L.qlin_gemm.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _I,
                                 ctypes.POINTER(qlin_config), _P, _SZ, _P]
         L.qlin_linear.argtypes = [_I, _I, _I, _I, _P, _I64, _P, _P, _P, _P, _P, _I,
@@ -151,6 +157,11 @@ def _check(st: int, what: str, raise_on_error: bool):
 def qlin_quantize_act(fmt, M, K, x, ldx, xq, x_scales, stream=None, raise_on_error=True):
     st = lib().qlin_quantize_act(fmt, M, K, _ptr(x), ldx, _ptr(xq), _ptr(x_scales), _stream(stream))
     return _check(st, "qlin_quantize_act", raise_on_error)
+
+
+def qlin_quantize_act_cfg(fmt, M, K, x, ldx, xq, x_scales, threads, stream=None, raise_on_error=True):
+    st = lib().qlin_quantize_act_cfg(fmt, M, K, _ptr(x), ldx, _ptr(xq), _ptr(x_scales), threads, _stream(stream))
+    return _check(st, "qlin_quantize_act_cfg", raise_on_error)
 
 
 def qlin_quantize_weight(fmt, N, K, w, wq, w_scales, stream=None, raise_on_error=True):

@@ -86,20 +86,22 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     if (c.waves < 1 || c.waves > kMaxWaves) return QLIN_ERR_INVALID_ARG;
     if (c.k_waves < 1 || c.k_waves > c.waves || c.waves % c.k_waves != 0) return QLIN_ERR_INVALID_ARG;
     if (c.reduce != 0 && c.reduce != 1) return QLIN_ERR_INVALID_ARG;
-    if (c.fuse_quant != 0 && c.fuse_quant != 1) return QLIN_ERR_INVALID_ARG;
+    if (c.act_path < QLIN_ACT_STAGED || c.act_path > QLIN_ACT_DIRECT) return QLIN_ERR_INVALID_ARG;
     // int8 sums (K <= 133120) and fp8 sums in units of 2^-18 stay below 2^51
     // in magnitude while K <= 40960: only those partials can be added as
     // packed 64-bit integers
     if (c.reduce == 1 && !(fmt == QLIN_W8A8_INT8 || (fmt == QLIN_FP8_DYNAMIC && K <= 40960)))
         return QLIN_ERR_INVALID_ARG;
-    const bool fuse = fused && c.fuse_quant == 1;
-    if (c.fuse_quant == 1 && c.tile_m != 16) return QLIN_ERR_INVALID_ARG;
+    const bool fuse = fused && c.act_path == QLIN_ACT_FUSED;
+    const bool direct = c.act_path == QLIN_ACT_DIRECT;
+    if (c.act_path == QLIN_ACT_FUSED && c.tile_m != 16) return QLIN_ERR_INVALID_ARG;
+    if (direct && c.tile_m >= 64) return QLIN_ERR_INVALID_ARG;
     if (c.tile_m >= 64) {
         // The large-M kernel: 128-channel tiles, 4 waves in a 2 x 2 grid,
         // Standard operand roles, slice reduction, static LDS.
         if (c.tile_n != 128 || c.waves != 4 || c.k_waves != 1 || c.swap_ab != 0 || c.reduce != 0)
             return QLIN_ERR_INVALID_ARG;
-        if (!gemm_variant_exists(fmt, c.tile_m, 0, 0)) return QLIN_ERR_INVALID_ARG;
+        if (!gemm_variant_exists(fmt, false, c.tile_m, 0, 0)) return QLIN_ERR_INVALID_ARG;
         p->tile_m = c.tile_m;
         p->tile_n = 128;
         p->sub_rows = 16;
@@ -155,7 +157,7 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     const int64_t wgs = (int64_t)((N + c.tile_n - 1) / c.tile_n) * ((M + c.tile_m - 1) / c.tile_m) * p->nsplit;
     const int budget = !grouped && wgs <= kComputeUnits ? kLdsBudgetOnePerCU : kLdsBudget;
     int pb = (budget - rows * 16) / per_block;
-    if (pb > p->kb_per_split) pb = p->kb_per_split;
+    if (pb > p->kb_per_split || direct) pb = p->kb_per_split;   // direct: nothing staged, one phase
     p->phase_blocks = pb;
     // In-kernel quantization: one phase (the workgroup's K range fits the
     // LDS), and the tile's activation chunks of 8 values, spread over the
@@ -171,9 +173,10 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
         xc = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
         if (xc == 0) return QLIN_ERR_INVALID_ARG;
     }
+    if (direct) xc = -1;
     p->xc = xc;
-    if (!gemm_variant_exists(fmt, c.tile_m, nr, xc)) return QLIN_ERR_INVALID_ARG;
-    size_t lds = (size_t)pb * per_block + (size_t)rows * 16;
+    if (!gemm_variant_exists(fmt, c.swap_ab != 0, c.tile_m, nr, xc)) return QLIN_ERR_INVALID_ARG;
+    size_t lds = direct ? 0 : (size_t)pb * per_block + (size_t)rows * 16;
     const size_t red = (size_t)(c.k_waves - 1) * nw * nr * mt * 64 * 16;
     if (red > lds) lds = red;
     p->lds_bytes = lds;
@@ -201,6 +204,20 @@ qlin_status qlin_quantize_act(qlin_format fmt, int M, int K, const void *x, int6
     if (M == 0) return QLIN_OK;
     return hip_status(launch_quant_act(fmt, M, K, x, ldx, xq, x_scales,
                                        static_cast<hipStream_t>(stream)));
+}
+
+qlin_status qlin_quantize_act_cfg(qlin_format fmt, int M, int K, const void *x, int64_t ldx, void *xq,
+                                  float *x_scales, int threads, void *stream) {
+    if (!fmt_ok(fmt)) return QLIN_ERR_INVALID_ARG;
+    if (threads != 0 && !quant_threads_valid(fmt, threads)) return QLIN_ERR_INVALID_ARG;
+    if (M < 0 || M > kMaxDim || K < 16 || K > kMaxDim || K % 16 != 0) return QLIN_ERR_SHAPE;
+    if (fmt == QLIN_BLOCK_FP8 && K % kGroup != 0) return QLIN_ERR_SHAPE;
+    if (ldx < K || ldx % 8 != 0) return QLIN_ERR_ALIGNMENT;
+    if (!x || !xq || !x_scales) return QLIN_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scales)) return QLIN_ERR_ALIGNMENT;
+    if (M == 0) return QLIN_OK;
+    return hip_status(launch_quant_act(fmt, M, K, x, ldx, xq, x_scales, static_cast<hipStream_t>(stream),
+                                       threads));
 }
 
 qlin_status qlin_quantize_weight(qlin_format fmt, int N, int K, const float *w, void *wq,
@@ -331,7 +348,7 @@ qlin_status qlin_gemm(qlin_format fmt, int M, int N, int K, const void *xq, cons
     GemmLaunch g = launch_args(p, M, N, K, wq, wpk, w_scales, y, out_type, workspace);
     g.xq = static_cast<const uint8_t *>(xq);
     g.xs = x_scales;
-    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, 0, g, p.lds_bytes,
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, p.xc, g, p.lds_bytes,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -350,7 +367,7 @@ static qlin_status plan_linear(qlin_format fmt, int M, int N, int K, const void 
     // the in-kernel quantization addresses the tile's rows of x with 32-bit
     // byte offsets; a very wide row stride takes the two-kernel path
     if (p->fuse && ((int64_t)((M < c->tile_m ? M : c->tile_m) - 1) * ldx + K) * 2 >= ((int64_t)1 << 31)) {
-        c->fuse_quant = 0;
+        c->act_path = QLIN_ACT_STAGED;
         st = make_plan(fmt, M, N, K, *c, true, p);
         if (st != QLIN_OK) return st;
     }
@@ -457,7 +474,7 @@ static qlin_status grouped_plan(qlin_format fmt, int groups, int N, int K, int t
     if (cfg) *c = *cfg;
     else grouped_default_config(max_group_rows, K, c);
     // the skinny kernel only (16- or 32-token tiles), codes quantized beforehand
-    if (c->tile_m > 32 || c->fuse_quant != 0) return QLIN_ERR_INVALID_ARG;
+    if (c->tile_m > 32 || c->act_path == QLIN_ACT_FUSED) return QLIN_ERR_INVALID_ARG;
     st = make_plan(fmt, max_group_rows, N, K, *c, false, p, true);
     if (st != QLIN_OK) return st;
     p->m_tiles = (int)std::min<int64_t>(grouped_grid_y(groups, total_rows, std::min(c->tile_m, max_group_rows)),
@@ -521,7 +538,7 @@ qlin_status qlin_grouped_gemm(qlin_format fmt, int groups, int N, int K, const i
     g.groups = groups;
     g.group_rows = std::min(c.tile_m, max_group_rows);
     g.m_tiles = p.m_tiles;   // grid y
-    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, 0, g, p.lds_bytes,
+    return hip_status(launch_gemm(fmt, c.swap_ab != 0, c.tile_m, p.nr, p.xc, g, p.lds_bytes,
                                   static_cast<hipStream_t>(stream)));
 }
 

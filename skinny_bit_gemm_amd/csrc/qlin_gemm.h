@@ -331,6 +331,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     typedef typename AccT<FMT>::type acc_t;
     typedef typename AccT<FMT>::scalar acc_s;
     constexpr bool FUSE = XC > 0;
+    // direct activations: codes quantized beforehand, each wave loads its
+    // own fragments with the weight slot they multiply (no LDS staging)
+    constexpr bool DIRECT = XC < 0;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
     __shared__ float s_rowscale[16 * MT];
@@ -412,6 +415,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     int lds_lo[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) lds_lo[mt] = ((mt * 16 + r16 < R ? mt * 16 + r16 : 0) * RS + 2 * quarter) * 16;
+    // direct activations: lane (r16, quarter) of fragment mt holds 32 bytes of
+    // the tile's token row 16 mt + r16 (codes row-major [M][K]; rows past R
+    // read out of range, i.e. zeros), and for the block format that row's
+    // scale of the block
+    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(g.xq + (int64_t)m0 * K, DIRECT ? (uint32_t)(R * K) : 0u);
+    const __amdgpu_buffer_rsrc_t asr =
+        buffer_rsrc(g.xs + (int64_t)m0 * G, DIRECT && FMT == FMT_BLOCK ? (uint32_t)(R * G * 4) : 0u);
+    uint32_t a_off[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a_off[mt] = (uint32_t)((mt * 16 + r16) * K + quarter * 32);
 
     acc_t acc[NR][MT];
 #pragma unroll
@@ -455,21 +468,32 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     // (the block scales come by buffer loads too, so that they count in the
     // same vector memory counter as the weights)
     const __amdgpu_buffer_rsrc_t bsr = buffer_rsrc(g.wsc, FMT == FMT_BLOCK ? (uint32_t)(N / kGroup * G * 4) : 0u);
-    auto issue = [&](v8i(&slot)[NR], float(&sws)[NR], int kb, bool live) {
+    v8i wbuf[PF][NR];
+    float wsbuf[PF][NR];
+    v8i abuf[DIRECT ? PF : 1][MT];      // direct activations: fragments of slot p
+    float asbuf[DIRECT ? PF : 1][MT];   // ... and (block format) their token scales
+    auto issue = [&](int p, int kb, bool live) {
         const int k = kb * kGroup;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            slot[r] = load_w(wrs[r], lane_off, kb, k + quarter * 32, K, live, wpk);
+            wbuf[p][r] = load_w(wrs[r], lane_off, kb, k + quarter * 32, K, live, wpk);
             if constexpr (FMT == FMT_BLOCK) {
                 const int soff = __builtin_amdgcn_readfirstlane(
                     ((min(nsub[r], N - 1) / kGroup) * G + min(kb, G - 1)) * 4);
-                sws[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bsr, 0, soff, 0));
+                wsbuf[p][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bsr, 0, soff, 0));
+            }
+        }
+        if constexpr (DIRECT) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                abuf[p][mt] = load_w(ars, a_off[mt], kb, k + quarter * 32, K, live, false);
+                if constexpr (FMT == FMT_BLOCK)
+                    asbuf[p][mt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        asr, live ? (uint32_t)(((mt * 16 + r16) * G + kb) * 4) : kOutOfRange, 0, 0));
             }
         }
     };
 
-    v8i wbuf[PF][NR];
-    float wsbuf[PF][NR];
     const int kstep = g.kw;
 
     for (int pb0 = kb_begin; pb0 < kb_end; pb0 += g.phase_blocks) {
@@ -509,7 +533,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                 xr[i] = load16(xrs, ok ? (uint32_t)((row * g.ldx + (c_lo + c) * 8) * 2) : kOutOfRange);
                 next_slot(row, c);
             }
-        } else {
+        } else if constexpr (!DIRECT) {
             // the codes go from memory straight into the LDS staging layout:
             // a 16-byte buffer load with the LDS bit writes lane l's data 16 l
             // bytes past the wave's LDS address, so one request copies 64
@@ -564,7 +588,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         prefetch_scales();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int p = 0; p < PF; ++p) issue(wbuf[p], wsbuf[p], pb0 + kw + p * kstep, p < nmine);
+        for (int p = 0; p < PF; ++p) issue(p, pb0 + kw + p * kstep, p < nmine);
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- 3. activations into LDS
@@ -629,7 +653,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                     next_slot(row, c);
                 }
             }
-        } else {
+        } else if constexpr (!DIRECT) {
             // this thread's staging loads are done once at most the younger
             // requests (the first batch of weight slots: two loads per
             // sub-tile and slot, and the block format's block scale) are
@@ -639,7 +663,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             static_assert(younger < 64, "vmcnt holds at most 63");
             __builtin_amdgcn_s_waitcnt(vmcnt_only(younger));
         }
-        __syncthreads();
+        if constexpr (!DIRECT) __syncthreads();
 
         // ---- 4. the weight stream
         // one block: MFMAs of the weights in slot p against this wave's block
@@ -652,10 +676,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
             v8i xf[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bool live = mt * 16 + r16 < R;
-                const uint4 lo = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + boff);
-                const uint4 hi = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + 16 + boff);
-                xf[mt] = join(select4(live, lo), select4(live, hi));
+                if constexpr (DIRECT) {
+                    xf[mt] = abuf[p][mt];
+                } else {
+                    const bool live = mt * 16 + r16 < R;
+                    const uint4 lo = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + boff);
+                    const uint4 hi = *reinterpret_cast<const uint4 *>(smem + lds_lo[mt] + 16 + boff);
+                    xf[mt] = join(select4(live, lo), select4(live, hi));
+                }
             }
             if constexpr (FMT == FMT_BLOCK) {
 #pragma unroll
@@ -668,7 +696,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
                         const float *sc = s_scale + b * R;
                         if (SWAP) {
                             const int row = mt * 16 + r16;
-                            const float c = (row < R ? sc[row] : 0.0f) * swv;
+                            float sa;
+                            if constexpr (DIRECT) sa = asbuf[p][mt];   // 0 past R (read out of range)
+                            else sa = row < R ? sc[row] : 0.0f;
+                            const float c = sa * swv;
 #pragma unroll
                             for (int i = 0; i < 4; ++i) acc[r][mt][i] += t[i] * c;
                         } else {
@@ -704,7 +735,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
 #pragma unroll
             for (int p = 0; p < PF; ++p) {
                 compute(p, j + p);
-                issue(wbuf[p], wsbuf[p], pb0 + kw + (j + PF + p) * kstep, j + PF + p < nmine);
+                issue(p, pb0 + kw + (j + PF + p) * kstep, j + PF + p < nmine);
             }
         }
 #pragma unroll
@@ -930,6 +961,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
 // the vector ALU; on its workload 4 measured ~3 % faster than 8, 6 in
 // between, 2 slower.  The other formats measured 3 % slower at 6.
 #define QLIN_PF_BLOCK(NR_, XC_) (NR_ >= 4 ? 1 : 4 / NR_)
+// direct activations hold a slot's activation fragments too: half the depth
+// at 32-token tiles
+#define QLIN_PF_DIRECT(PF_, MT_) ((PF_) / (MT_) > 0 ? (PF_) / (MT_) : 1)
 
 typedef void (*gemm_fn)(GemmLaunch);
 

@@ -13,12 +13,17 @@ static gemm_fn pick(int tile_m, int nr, int xc) {
         return tile_m == 64 ? gemm_big_kernel<FMT_FP8, 64> : gemm_big_kernel<FMT_FP8, 128>;
     }
 #define QLIN_PICK(MT_, NR_, XC_) \
-    if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_) return gemm_kernel<FMT_FP8, SWAP, MT_, NR_, QLIN_PF(NR_, XC_), XC_>;
+    if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_)                                               \
+        return gemm_kernel<FMT_FP8, SWAP, MT_, NR_,                                                   \
+                           (XC_ < 0 ? QLIN_PF_DIRECT(QLIN_PF(NR_, XC_), MT_) : QLIN_PF(NR_, XC_)), XC_>;
     QLIN_PICK(1, 1, 0) QLIN_PICK(1, 2, 0) QLIN_PICK(1, 4, 0)
     QLIN_PICK(2, 1, 0) QLIN_PICK(2, 2, 0) QLIN_PICK(2, 4, 0)
     QLIN_PICK(1, 1, 2) QLIN_PICK(1, 2, 2) QLIN_PICK(1, 4, 2)
     QLIN_PICK(1, 1, 4) QLIN_PICK(1, 2, 4) QLIN_PICK(1, 4, 4)
     QLIN_PICK(1, 1, 8) QLIN_PICK(1, 2, 8) QLIN_PICK(1, 4, 8)
+    // direct activations (xc = -1)
+    QLIN_PICK(1, 1, -1) QLIN_PICK(1, 2, -1) QLIN_PICK(1, 4, -1)
+    QLIN_PICK(2, 1, -1) QLIN_PICK(2, 2, -1) QLIN_PICK(2, 4, -1)
 #undef QLIN_PICK
     return nullptr;
 }

@@ -76,12 +76,13 @@ struct Plan {
     int packed;           // split-K reduction through packed 64-bit atomics
     int fuse;             // activation quantization inside the GEMM kernel
     int xc;               // ... with this many 8-value chunks per lane in registers
+                          // (-1: direct activation fragments, no LDS staging)
     size_t ws_bytes;          // workspace bytes (0 without split)
     size_t ws_counter_bytes;  // of which arrival counters (the rest: sums)
 };
 
 // Fills *plan; returns QLIN_OK or the reason the schedule is invalid.
-// `fused`: planned for qlin_linear (cfg.fuse_quant applies) or qlin_gemm.
+// `fused`: planned for qlin_linear (cfg.act_path applies) or qlin_gemm.
 // `grouped`: for a grouped launch, whose grid is not the plan's own (its
 // workgroups keep the smaller LDS budget).
 qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &cfg, bool fused,
@@ -95,16 +96,21 @@ int token_bucket(int M);
 bool strict_mode();
 
 // Kernel launchers (qlin_kernels.hip); they only enqueue.
+// threads: per token row (per-token formats: 64, 128, 256 or 512) or per
+// workgroup (1x128 groups: 64 or 256); 0 = quant_threads_rule
 hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, void *xq,
-                            float *xs, hipStream_t s);
+                            float *xs, hipStream_t s, int threads = 0);
+int quant_threads_rule(int fmt, int M, int K);
+bool quant_threads_valid(int fmt, int threads);
 hipError_t launch_quant_weight(int fmt, int N, int K, const float *w, void *wq, float *ws,
                                hipStream_t s);
 // [batch][N][K] row-major codes -> [batch][packed_weight_bytes(N, K)]
 hipError_t launch_pack_weight(int batch, int N, int K, const void *wq, void *out, hipStream_t s);
-// xc: register chunks per lane of the in-kernel quantization (0: unfused)
+// xc: register chunks per lane of the in-kernel quantization (0: codes
+// staged in LDS; -1: direct, each wave loads its own activation fragments)
 hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, int xc, const GemmLaunch &g,
                        size_t lds_bytes, hipStream_t s);
-bool gemm_variant_exists(int fmt, int tile_m, int nr, int xc);
+bool gemm_variant_exists(int fmt, bool swap, int tile_m, int nr, int xc);
 // this device's static scratch array (kScratchBytes, zero between calls);
 // see qlin_linear_scratch
 hipError_t static_scratch(hipStream_t s, void **out);

@@ -14,65 +14,74 @@
 
 namespace qlin {
 
-constexpr int kQuantThreads = 512;
-
-// One workgroup per token.  With CPT > 0 every thread keeps its (at most
-// CPT) 16-byte chunks of the row in registers: one read of the row, the
-// row's amax by a wave reduction and one across waves, then the codes.
-// CPT == 0 is the fallback for very long rows: the row is read twice.
-template <int FMT, int CPT>
-__global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(const uint16_t *__restrict__ x,
-                                                                    int64_t ldx, int K,
-                                                                    uint8_t *__restrict__ xq,
-                                                                    float *__restrict__ xs) {
-    __shared__ float red[kQuantThreads / 64];
-    const int m = blockIdx.x;
-    const uint16_t *row = x + (int64_t)m * ldx;
-    uint8_t *qrow = xq + (int64_t)m * K;
-    const int nch = K >> 3;
+// One token row per TPR threads (TPR / 64 waves), max(1, 256 / TPR) rows per
+// workgroup.  With CPT > 0 every thread keeps its (at most CPT) 16-byte
+// chunks of the row in registers: one read of the row, the row's amax by a
+// wave reduction (and, for more than one wave per row, one across the row's
+// waves through LDS), then the codes.  CPT == 0 is the fallback for rows
+// longer than CPT chunks per thread allow: the row is read twice.  One wave
+// per row needs no LDS and no barrier; more waves per row cut each thread's
+// share of the row (fewer chunks to convert one after another).
+template <int FMT, int TPR, int CPT>
+__global__ __launch_bounds__(TPR >= 256 ? TPR : 256) void quant_token_kernel(const uint16_t *__restrict__ x,
+                                                                            int64_t ldx, int M, int K,
+                                                                            uint8_t *__restrict__ xq,
+                                                                            float *__restrict__ xs) {
+    constexpr int RPW = TPR >= 256 ? 1 : 256 / TPR;   // rows per workgroup
+    constexpr int WPR = TPR / 64;                      // waves per row
+    __shared__ float red[RPW * WPR];
+    const int t = threadIdx.x % TPR, rsub = threadIdx.x / TPR;
+    const int m = blockIdx.x * RPW + rsub;
+    const bool live = m < M;
+    const uint16_t *row = x + (int64_t)(live ? m : 0) * ldx;
+    uint8_t *qrow = xq + (int64_t)(live ? m : 0) * K;
+    const int nch = live ? K >> 3 : 0;
     float amax = 0.0f;
     uint4 v[CPT > 0 ? CPT : 1];
     if constexpr (CPT > 0) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const int c = threadIdx.x + j * kQuantThreads;
+            const int c = t + j * TPR;
             v[j] = c < nch ? *reinterpret_cast<const uint4 *>(row + c * 8) : make_uint4(0, 0, 0, 0);
             amax = fmaxf(amax, absmax8(v[j]));
         }
     } else {
-        for (int c = threadIdx.x; c < nch; c += kQuantThreads)
+        for (int c = t; c < nch; c += TPR)
             amax = fmaxf(amax, absmax8(*reinterpret_cast<const uint4 *>(row + c * 8)));
     }
     amax = wave_max(amax);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = red[0];
+    if constexpr (WPR > 1) {
+        if ((t & 63) == 0) red[rsub * WPR + (t >> 6)] = amax;
+        __syncthreads();
+        amax = red[rsub * WPR];
 #pragma unroll
-    for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+        for (int w = 1; w < WPR; ++w) amax = fmaxf(amax, red[rsub * WPR + w]);
+    }
+    if (!live) return;
     const float s = amax == 0.0f ? 0.0f : amax / qmax_of<FMT>();
     const float y = recip_scale(s);
-    if (threadIdx.x == 0) xs[m] = s;
+    if (t == 0) xs[m] = s;
     if constexpr (CPT > 0) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const int c = threadIdx.x + j * kQuantThreads;
+            const int c = t + j * TPR;
             if (c < nch) *reinterpret_cast<uint2 *>(qrow + c * 8) = quant8<FMT>(v[j], s, y);
         }
     } else {
-        for (int c = threadIdx.x; c < nch; c += kQuantThreads)
+        for (int c = t; c < nch; c += TPR)
             *reinterpret_cast<uint2 *>(qrow + c * 8) =
                 quant8<FMT>(*reinterpret_cast<const uint4 *>(row + c * 8), s, y);
     }
 }
 
 // Per (token, 128-wide K group): 16 lanes own one group, 8 values each; a
-// 256-thread workgroup covers 16 groups.
-__global__ __launch_bounds__(256) void quant_group_kernel(const uint16_t *__restrict__ x,
-                                                          int64_t ldx, int M, int K,
-                                                          uint8_t *__restrict__ xq,
-                                                          float *__restrict__ xs) {
+// workgroup of 16 GPW threads covers GPW groups.
+template <int GPW>
+__global__ __launch_bounds__(16 * GPW) void quant_group_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                               int M, int K, uint8_t *__restrict__ xq,
+                                                               float *__restrict__ xs) {
     const int G = K / kGroup;
-    const int gi = blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int gi = blockIdx.x * GPW + (threadIdx.x >> 4);
     const int j = threadIdx.x & 15;
     const bool live = gi < M * G;
     const int m = live ? gi / G : 0;
@@ -187,32 +196,61 @@ hipError_t launch_pack_weight(int batch, int N, int K, const void *wq, void *out
     return hipGetLastError();
 }
 
+// Threads per token row (per-token formats) or per workgroup (1x128
+// groups) of the quantize kernels when the caller does not choose.
+int quant_threads_rule(int fmt, int M, int K) {
+    (void)M;
+    (void)K;
+    return fmt == FMT_BLOCK ? 256 : 512;
+}
+
+bool quant_threads_valid(int fmt, int threads) {
+    if (fmt == FMT_BLOCK) return threads == 64 || threads == 256;
+    return threads == 64 || threads == 128 || threads == 256 || threads == 512;
+}
+
+template <int F, int TPR>
+static void launch_token(int M, int K, const uint16_t *xb, int64_t ldx, uint8_t *q, float *xs, hipStream_t s) {
+    constexpr int RPW = TPR >= 256 ? 1 : 256 / TPR;
+    const dim3 grid((M + RPW - 1) / RPW), block(TPR >= 256 ? TPR : 256);
+    const int cpt = (K / 8 + TPR - 1) / TPR;
+#define QLIN_QT(C) hipLaunchKernelGGL((quant_token_kernel<F, TPR, C>), grid, block, 0, s, xb, ldx, M, K, q, xs)
+    if (cpt <= 1) QLIN_QT(1);
+    else if (cpt <= 2) QLIN_QT(2);
+    else if (cpt <= 4) QLIN_QT(4);
+    else if (cpt <= 8) QLIN_QT(8);
+    else if (cpt <= 16 && TPR <= 128) QLIN_QT(16);
+    else QLIN_QT(0);
+#undef QLIN_QT
+}
+
+template <int F>
+static void launch_token_any(int threads, int M, int K, const uint16_t *xb, int64_t ldx, uint8_t *q, float *xs,
+                             hipStream_t s) {
+    switch (threads) {
+    case 64: launch_token<F, 64>(M, K, xb, ldx, q, xs, s); break;
+    case 128: launch_token<F, 128>(M, K, xb, ldx, q, xs, s); break;
+    case 256: launch_token<F, 256>(M, K, xb, ldx, q, xs, s); break;
+    default: launch_token<F, 512>(M, K, xb, ldx, q, xs, s); break;
+    }
+}
+
 hipError_t launch_quant_act(int fmt, int M, int K, const void *x, int64_t ldx, void *xq,
-                            float *xs, hipStream_t s) {
+                            float *xs, hipStream_t s, int threads) {
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     uint8_t *q = static_cast<uint8_t *>(xq);
+    if (threads == 0) threads = quant_threads_rule(fmt, M, K);
     if (fmt == FMT_BLOCK) {
         const int groups = M * (K / kGroup);
-        hipLaunchKernelGGL(quant_group_kernel, dim3((groups + 15) / 16), dim3(256), 0, s, xb, ldx,
-                           M, K, q, xs);
+        if (threads == 64)
+            hipLaunchKernelGGL(quant_group_kernel<4>, dim3((groups + 3) / 4), dim3(64), 0, s, xb, ldx, M, K, q, xs);
+        else
+            hipLaunchKernelGGL(quant_group_kernel<16>, dim3((groups + 15) / 16), dim3(256), 0, s, xb, ldx, M, K, q,
+                               xs);
+    } else if (fmt == FMT_I8) {
+        launch_token_any<FMT_I8>(threads, M, K, xb, ldx, q, xs, s);
     } else {
-        const int nch = K / 8;
-        const int cpt = (nch + kQuantThreads - 1) / kQuantThreads;
-#define QLIN_QT(F, C) \
-    hipLaunchKernelGGL((quant_token_kernel<F, C>), dim3(M), dim3(kQuantThreads), 0, s, xb, ldx, K, q, xs)
-#define QLIN_QT_ALL(F)                  \
-    if (cpt <= 1) QLIN_QT(F, 1);        \
-    else if (cpt <= 2) QLIN_QT(F, 2);   \
-    else if (cpt <= 4) QLIN_QT(F, 4);   \
-    else if (cpt <= 8) QLIN_QT(F, 8);   \
-    else QLIN_QT(F, 0);
-        if (fmt == FMT_I8) {
-            QLIN_QT_ALL(FMT_I8)
-        } else {
-            QLIN_QT_ALL(FMT_FP8)
-        }
-#undef QLIN_QT_ALL
-#undef QLIN_QT
+        launch_token_any<FMT_FP8>(threads, M, K, xb, ldx, q, xs, s);
     }
     return hipGetLastError();
 }
@@ -292,11 +330,11 @@ hipError_t static_scratch(hipStream_t s, void **out) {
     return hipSuccess;
 }
 
-bool gemm_variant_exists(int fmt, int tile_m, int nr, int xc) {
+bool gemm_variant_exists(int fmt, bool swap, int tile_m, int nr, int xc) {
     switch (fmt) {
-    case FMT_FP8: return gemm_pick_fp8(false, tile_m, nr, xc) != nullptr;
-    case FMT_I8: return gemm_pick_i8(false, tile_m, nr, xc) != nullptr;
-    case FMT_BLOCK: return gemm_pick_block(false, tile_m, nr, xc) != nullptr;
+    case FMT_FP8: return gemm_pick_fp8(swap, tile_m, nr, xc) != nullptr;
+    case FMT_I8: return gemm_pick_i8(swap, tile_m, nr, xc) != nullptr;
+    case FMT_BLOCK: return gemm_pick_block(swap, tile_m, nr, xc) != nullptr;
     }
     return false;
 }

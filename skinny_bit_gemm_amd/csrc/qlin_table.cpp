@@ -12,7 +12,7 @@
 // Table format (text, '#' starts a comment):
 //   qlin-table <abi version> <gfx arch>
 //   <format> <N> <K> <M bucket> <swap_ab> <split_k> <tile_m> <tile_n> <waves> <k_waves>
-//            <reduce> <fuse_quant>
+//            <reduce> <act_path>
 // with <format> one of fp8_dynamic, w8a8_int8, block_fp8.
 #include <dlfcn.h>
 
@@ -158,8 +158,8 @@ qlin_status table_lookup(qlin_format fmt, int M, int N, int K, qlin_config *out,
 // |log2 N/N'| + |log2 K/K'|, plus 1/2 for an entry of another per-token
 // format (the fp8 and int8 schedules stream the same bytes) and 1 between
 // the per-token and the block-scaled formats.  An entry whose configuration
-// does not fit the shape is passed over (a fused one first drops the fused
-// quantization).
+// does not fit the shape is passed over (one with fused or direct
+// activations first falls back to staged ones).
 qlin_status table_nearest(qlin_format fmt, int M, int N, int K, qlin_config *out, bool *found) {
     TableState &s = state();
     std::lock_guard<std::mutex> lk(s.mu);
@@ -177,8 +177,8 @@ qlin_status table_nearest(qlin_format fmt, int M, int N, int K, qlin_config *out
         qlin_config c = e.second;
         Plan p;
         if (make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) {
-            if (!c.fuse_quant) continue;
-            c.fuse_quant = 0;
+            if (c.act_path == QLIN_ACT_STAGED) continue;
+            c.act_path = QLIN_ACT_STAGED;
             if (make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) continue;
         }
         best = d;
@@ -220,9 +220,9 @@ void default_config(qlin_format fmt, int M, int N, int K, qlin_config *out) {
     c.split_k = split;
     c.swap_ab = split >= 4 ? 1 : 0;
     c.reduce = 0;
-    c.fuse_quant = M <= 4 && c.tile_m == 16 ? 1 : 0;
+    c.act_path = M <= 4 && c.tile_m == 16 ? QLIN_ACT_FUSED : QLIN_ACT_STAGED;
     Plan p;
-    if (c.fuse_quant && make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) c.fuse_quant = 0;
+    if (c.act_path == QLIN_ACT_FUSED && make_plan(fmt, M, N, K, c, true, &p) != QLIN_OK) c.act_path = QLIN_ACT_STAGED;
     *out = c;
 }
 

@@ -10,8 +10,10 @@ graph replay).  Here the search is exhaustive over a fixed candidate grid
 hipGraph of back-to-back layers (qlin_linear: quantize + GEMM) over distinct
 weight copies (>= 1 GiB in total, so the Infinity Cache cannot hold them),
 in the packed weight layout (--layout row-major for the other).
-A coarse pass over the schedule grid (each schedule with the quantization
-in its own kernel and fused into the GEMM), then the best few with each
+A coarse pass over the schedule grid (each schedule with each activation
+path: codes quantized in their own kernel and staged in the LDS, the same
+codes loaded by each wave directly, or quantized inside the GEMM), then the
+best few with each
 split-K reduction, then the best of those again with more replays.  With
 --merge, a point that already has an entry keeps it unless the new best beats
 it, timed beside it in the same session, by more than --keep-margin: the
@@ -57,9 +59,10 @@ def exact_format(fmt, K):
 
 
 def candidates(fmt, M, N, K):
-    """Base grid: schedule, tile, split and wave layout, each with the
-    quantization in a separate kernel and (where the tile's rows fit the
-    kernel's registers) inside the GEMM; slice reduction."""
+    """Base grid: schedule, tile, split and wave layout, each with staged
+    and with direct activation codes (quantized in a separate kernel) and,
+    where the tile's rows fit the kernel's registers, quantized inside the
+    GEMM; slice reduction."""
     nkb = -(-K // 128)
     seen = set()
     out = []
@@ -76,8 +79,9 @@ def candidates(fmt, M, N, K):
                 if wgs < 16 or wgs > 16384:
                     continue
                 seen.add(key)
-                for fuse in ((0, 1) if tile_m == 16 else (0,)):
-                    c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, fuse)
+                acts = (q.QLIN_ACT_STAGED, q.QLIN_ACT_DIRECT) + ((q.QLIN_ACT_FUSED,) if tile_m == 16 else ())
+                for act in acts:
+                    c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, act)
                     if q.qlin_validate_config(fmt, M, N, K, c) == 0:
                         out.append(c)
     if M > 32:
@@ -99,7 +103,7 @@ def variants(fmt, M, N, K, c):
     out = []
     reds = [0, 1] if (c.split_k > 1 and exact_format(fmt, K)) else [0]
     for r in reds:
-        v = q.make_config(c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves, r, c.fuse_quant)
+        v = q.make_config(c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves, r, c.act_path)
         if q.qlin_validate_config(fmt, M, N, K, v) == 0:
             out.append(v)
     return out
@@ -242,7 +246,7 @@ def tune_point(fmt, M, N, K, keep=10, final=5, incumbent=None, margin=0.0):
 
 STANDARD_HEADER = (
     "# measured on MI355X by skinny_bit_gemm_amd.tune (hipGraph replay, rotating weights)",
-    "# format N K M swap_ab split_k tile_m tile_n waves k_waves reduce fuse_quant",
+    "# format N K M swap_ab split_k tile_m tile_n waves k_waves reduce act_path",
     "# (times are of the whole layer, quantize + GEMM; best_by_class in the report",
     "#  compares the schedules' best coarse times, slice reduction)",
 )
@@ -320,7 +324,7 @@ def main(argv=None):
             (t, c), by_class, n, kept = tune_point(fmt, M, N, K, incumbent=inc, margin=args.keep_margin)
             gbs = algorithmic_bytes(fmt, M, N, K) / t / 1e3
             entries[(fname, N, K, M)] = [str(v) for v in (c.swap_ab, c.split_k, c.tile_m, c.tile_n,
-                                                         c.waves, c.k_waves, c.reduce, c.fuse_quant)]
+                                                         c.waves, c.k_waves, c.reduce, c.act_path)]
             rec = {"fmt": fname, "N": N, "K": K, "M": M, "us": round(t, 3), "GBps": round(gbs, 1),
                    "cfg": c.as_dict(), "candidates": n, "kept_existing_entry": kept,
                    "best_by_class": {k: {"us": round(v[0], 3), "cfg": v[1].as_dict()}

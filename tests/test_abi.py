@@ -107,6 +107,21 @@ def test_linear_scratch_checks_before_any_hip_call():
     assert call(M=0) == OK
 
 
+def test_quantize_act_cfg_checks_before_any_hip_call():
+    def call(fmt=FP8, M=4, K=512, threads=64):
+        return q.qlin_quantize_act_cfg(fmt, M, K, A, K, A, A, threads, stream=0, raise_on_error=False)
+    for t in (0, 64, 128, 256, 512):
+        assert call(M=0, threads=t) == OK
+        assert call(fmt=I8, M=0, threads=t) == OK
+    for t in (0, 64, 256):
+        assert call(fmt=BLK, M=0, threads=t) == OK
+    for t in (-1, 32, 96, 1024):
+        assert call(threads=t) == EINVAL
+    assert call(fmt=BLK, threads=128) == EINVAL
+    assert call(fmt=BLK, threads=512) == EINVAL
+    assert call(K=520) == ESHAPE
+
+
 def test_pack_weight_checks_before_any_hip_call():
     assert q.qlin_packed_weight_bytes(48, 1040) == 48 * 9 * 128      # blocks of 128 K, zero-padded
     assert q.qlin_packed_weight_bytes(4096, 2048) == 4096 * 2048
@@ -153,8 +168,32 @@ def test_gemm_rejects_bad_configs():
               q.make_config(tile_n=48, waves=3, k_waves=1), q.make_config(tile_n=96, waves=6, k_waves=2),
               q.make_config(tile_n=96, waves=6, k_waves=1), q.make_config(tile_n=40, waves=5, k_waves=1),
               q.make_config(tile_n=80, waves=5, k_waves=1), q.make_config(tile_n=224, waves=7, k_waves=1),
-              q.make_config(tile_n=56, waves=7, k_waves=1, fuse_quant=1)):
+              q.make_config(tile_n=56, waves=7, k_waves=1, act_path=1)):
         assert q.qlin_validate_config(FP8, 4, 256, 512, c) == OK, c
+
+
+def test_activation_paths():
+    """act_path: the header's values, the range check, and where each path
+    exists (direct loads: the skinny kernel only, the block format in the
+    Swap-AB roles only; fused quantization: 16-token tiles)."""
+    with open(HEADER) as f:
+        text = f.read()
+    for name in ("QLIN_ACT_STAGED", "QLIN_ACT_FUSED", "QLIN_ACT_DIRECT"):
+        assert f"#define {name} {getattr(q, name)}" in text, name
+    assert q.qlin_validate_config(FP8, 4, 256, 512, q.make_config(act_path=3)) == EINVAL
+    assert q.qlin_validate_config(FP8, 4, 256, 512, q.make_config(act_path=-1)) == EINVAL
+    D = q.QLIN_ACT_DIRECT
+    for fmt in (FP8, I8):
+        for c in (q.make_config(0, 1, 16, 32, 4, 4, act_path=D), q.make_config(1, 2, 32, 64, 4, 2, act_path=D),
+                  q.make_config(0, 3, 16, 128, 8, 2, reduce=1, act_path=D),
+                  q.make_config(1, 1, 16, 8, 1, 1, act_path=D)):
+            assert q.qlin_validate_config(fmt, 20, 512, 2048, c) == OK, (fmt, c)
+            assert q.qlin_workspace_bytes(fmt, 20, 512, 2048, c) == \
+                q.qlin_workspace_bytes(fmt, 20, 512, 2048, q.make_config(**{**c.as_dict(), "act_path": 0}))
+    assert q.qlin_validate_config(BLK, 20, 512, 2048, q.make_config(1, 1, 16, 32, 4, 4, act_path=D)) == OK
+    assert q.qlin_validate_config(BLK, 20, 512, 2048, q.make_config(0, 1, 16, 32, 4, 4, act_path=D)) == EINVAL
+    assert q.qlin_validate_config(FP8, 300, 512, 2048, q.make_config(0, 1, 64, 128, 4, 1, act_path=D)) == EINVAL
+    assert q.qlin_validate_config(FP8, 20, 512, 2048, q.make_config(0, 1, 32, 32, 4, 4, act_path=1)) == EINVAL
 
 
 def test_large_m_configs():
@@ -167,7 +206,7 @@ def test_large_m_configs():
                 assert q.qlin_validate_config(fmt, 300, 512, 2048, q.make_config(0, split, tm, 128, 4, 1)) == OK
         bad = [q.make_config(1, 1, 128, 128, 4, 1), q.make_config(0, 1, 128, 64, 4, 1),
                q.make_config(0, 1, 128, 128, 8, 1), q.make_config(0, 1, 128, 128, 4, 4),
-               q.make_config(0, 2, 128, 128, 4, 1, reduce=1), q.make_config(0, 1, 128, 128, 4, 1, fuse_quant=1),
+               q.make_config(0, 2, 128, 128, 4, 1, reduce=1), q.make_config(0, 1, 128, 128, 4, 1, act_path=1),
                q.make_config(0, 1, 96, 128, 4, 1)]
         for c in bad:
             assert q.qlin_validate_config(fmt, 300, 512, 2048, c) == EINVAL, (fmt, c)
@@ -246,9 +285,9 @@ def test_default_rule_without_table_entries(tmp_path):
     assert q.qlin_table_entries() == 0
     c = q.qlin_select_variant(FP8, 3, 1024, 1024)
     assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.waves, c.k_waves, c.reduce) == (1, 4, 16, 64, 4, 2, 0)
-    assert c.fuse_quant == 1                      # 3 rows of 1024 values fit the registers
+    assert c.act_path == 1                      # 3 rows of 1024 values fit the registers
     c = q.qlin_select_variant(FP8, 32, 1024, 1024)
-    assert (c.split_k, c.tile_m, c.fuse_quant) == (4, 32, 0)
+    assert (c.split_k, c.tile_m, c.act_path) == (4, 32, 0)
     c = q.qlin_select_variant(I8, 4, 12288, 4096)  # 192 tiles already: no split
     assert (c.swap_ab, c.split_k) == (0, 1)
     c = q.qlin_select_variant(I8, 200, 4096, 4096)
@@ -264,7 +303,7 @@ def test_nearest_entry_for_unlisted_shapes(tmp_path):
     # same bucket only; a per-token format at distance 0 + 1/2 beats the same
     # format at distance 2
     c = q.qlin_select_variant(FP8, 3, 1024, 1024)
-    assert (c.swap_ab, c.split_k, c.tile_n, c.waves, c.k_waves, c.fuse_quant) == (1, 1, 64, 8, 4, 1)
+    assert (c.swap_ab, c.split_k, c.tile_n, c.waves, c.k_waves, c.act_path) == (1, 1, 64, 8, 4, 1)
     # nearer in N and K wins within the format
     c = q.qlin_select_variant(FP8, 4, 2048, 4096)
     assert (c.split_k, c.tile_n, c.reduce) == (2, 32, 1)
@@ -275,7 +314,20 @@ def test_nearest_entry_for_unlisted_shapes(tmp_path):
     # a fused entry whose rows do not fit the registers at this K loses the
     # fused quantization, not the rest
     c = q.qlin_select_variant(I8, 4, 1024, 65536)
-    assert (c.swap_ab, c.tile_n, c.waves, c.k_waves, c.fuse_quant) == (1, 64, 8, 4, 0)
+    assert (c.swap_ab, c.tile_n, c.waves, c.k_waves, c.act_path) == (1, 64, 8, 4, 0)
+    # a direct Standard entry has no block-format kernel: the block format
+    # keeps the schedule with staged activations
+    path = write_table(tmp_path, "fp8_dynamic 2048 2048 4 0 2 16 32 4 2 0 2\n")
+    assert q.qlin_load_table(path) == OK
+    c = q.qlin_select_variant(FP8, 4, 2048, 2048)
+    assert (c.swap_ab, c.split_k, c.tile_n, c.act_path) == (0, 2, 32, q.QLIN_ACT_DIRECT)
+    c = q.qlin_select_variant(BLK, 4, 2048, 2048)
+    assert (c.swap_ab, c.split_k, c.tile_n, c.act_path) == (0, 2, 32, q.QLIN_ACT_STAGED)
+    path = write_table(tmp_path,
+                       "fp8_dynamic 2048 2048 4 0 2 16 32 4 2 1 0\n"
+                       "w8a8_int8 1024 1024 4 1 1 16 64 8 4 0 1\n"
+                       "fp8_dynamic 1024 1024 8 1 2 16 64 4 2 0 0\n")
+    assert q.qlin_load_table(path) == OK
     # another bucket: its own entry, or the built-in rule when it has none
     c = q.qlin_select_variant(FP8, 8, 4096, 4096)
     assert (c.swap_ab, c.split_k, c.tile_n) == (1, 2, 64)
@@ -306,6 +358,8 @@ def test_strict_mode_missing_entry_is_an_error(tmp_path):
     ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 48 4 2 0 0\n"),     # invalid tile
     ("qlin-table 1 gfx950", "block_fp8 1024 1024 4 1 2 16 64 4 2 1 0\n"),  # packed: exact formats only
     ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 32 1 2 32 64 4 2 0 1\n"),  # fused needs tile_m 16
+    ("qlin-table 1 gfx950", "fp8_dynamic 1024 1024 4 1 2 16 64 4 2 0 3\n"),  # no such activation path
+    ("qlin-table 1 gfx950", "block_fp8 1024 1024 4 0 2 16 64 4 2 0 2\n"),  # direct block: Swap-AB only
     ("nonsense", ""),
 ])
 def test_corrupt_tables_are_rejected(tmp_path, header, body):
@@ -373,7 +427,7 @@ def test_grouped_gemm_validation():
     assert gg(cfg=split, ws=A, wsb=need - 1) == EWS
     assert gg(cfg=split, ws=None, wsb=need) == EWS
     c = q.qlin_grouped_select_variant(FP8, 128, 1536, 2048, 8)
-    assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.fuse_quant) == (1, 1, 16, 64, 0)
+    assert (c.swap_ab, c.split_k, c.tile_m, c.tile_n, c.act_path) == (1, 1, 16, 64, 0)
     assert q.qlin_grouped_select_variant(I8, 128, 2048, 768, 32).tile_m == 32
     c = q.qlin_grouped_select_variant(FP8, 128, 1536, 2048, 2)
     assert (c.tile_n, c.waves, c.k_waves) == (32, 4, 4)

@@ -33,8 +33,8 @@ def _gpu_ready():
     oracle.build()
 
 
-def cfg(swap=1, split=1, tile_m=16, tile_n=64, waves=4, k_waves=2, reduce=0):
-    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves, reduce, 0)
+def cfg(swap=1, split=1, tile_m=16, tile_n=64, waves=4, k_waves=2, reduce=0, act=0):
+    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves, reduce, act)
 
 
 SCHEDULES = {
@@ -49,6 +49,10 @@ SCHEDULES = {
     "odd48_w3": cfg(1, 1, 16, 48, 3, 1),
     "odd96_w6kw2_std_m32": cfg(0, 1, 32, 96, 6, 2),
     "odd40_w5_split2": cfg(1, 2, 16, 40, 5, 1),
+    # direct activation loads (no LDS staging): each group's rows start
+    # at its own offset, rows past the group read out of range
+    "direct_swap": cfg(1, 1, 16, 64, 4, 2, act=2),
+    "direct_swap_m32_split2": cfg(1, 2, 32, 64, 4, 2, act=2),
 }
 PACKED = {"packed2": cfg(1, 2, 16, 64, 4, 2, reduce=1), "packed4_std": cfg(0, 4, 16, 32, 4, 2, reduce=1),
           "packed2_half8": cfg(1, 2, 16, 8, 2, 2, reduce=1), "packed3_odd56_w7": cfg(1, 3, 16, 56, 7, 1, reduce=1)}
@@ -116,10 +120,11 @@ def test_grouped_packed_reduction(fmt, name):
 
 @pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=FMT_IDS[:2])
 @pytest.mark.parametrize("tile_m", [16, 32])
-def test_grouped_ragged_k_and_many_rows(fmt, tile_m):
+@pytest.mark.parametrize("act", [0, 2], ids=["staged", "direct"])
+def test_grouped_ragged_k_and_many_rows(fmt, tile_m, act):
     # K not a multiple of 128; 40 tokens top-2 of 4 experts: groups of 18 to
     # 25 rows, so several token tiles per group with a ragged last one
-    check_case(fmt, 4, 256, 1040, 40, 2, 3, cfg(1, 1, tile_m, 64, 4, 2))
+    check_case(fmt, 4, 256, 1040, 40, 2, 3, cfg(1, 1, tile_m, 64, 4, 2, act=act))
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)

@@ -33,8 +33,8 @@ def _gpu_ready():
     oracle.build()
 
 
-def cfg(swap=0, split=1, tile_m=16, tile_n=32, waves=4, k_waves=4, reduce=0, fuse=0):
-    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves, reduce, fuse)
+def cfg(swap=0, split=1, tile_m=16, tile_n=32, waves=4, k_waves=4, reduce=0, act=0):
+    return q.make_config(swap, split, tile_m, tile_n, waves, k_waves, reduce, act)
 
 
 # schedules every format is checked with: Standard, Swap-AB, Split-K (with
@@ -75,6 +75,21 @@ PACKED = {
     "packed3_half16_std": cfg(0, 3, 32, 16, 2, 1, reduce=1),
     "packed2_odd6_swap": cfg(1, 2, 16, 96, 6, 2, reduce=1),
     "packed3_odd7_half_std": cfg(0, 3, 32, 56, 7, 1, reduce=1),
+}
+
+# direct activations (codes quantized beforehand, each wave loading its own
+# fragments with the weight slot they multiply, nothing staged in the LDS);
+# the block format has them in the Swap-AB roles only
+DIRECT = {
+    "direct_swap": cfg(1, 1, 16, 32, 4, 4, act=2),
+    "direct_std": cfg(0, 1, 16, 32, 4, 4, act=2),
+    "direct_swap_m32": cfg(1, 1, 32, 64, 4, 2, act=2),
+    "direct_std_m32_odd6_kw2": cfg(0, 1, 32, 96, 6, 2, act=2),
+    "direct_split4_swap": cfg(1, 4, 16, 64, 4, 1, act=2),
+    "direct_nr4_m32": cfg(1, 2, 32, 64, 1, 1, act=2),
+    "direct_half8_swap": cfg(1, 1, 16, 8, 1, 1, act=2),
+    "direct_odd5_half_swap_split2": cfg(1, 2, 16, 40, 5, 1, act=2),
+    "direct_packed3_nw4": cfg(0, 3, 16, 128, 8, 2, reduce=1, act=2),
 }
 
 
@@ -137,6 +152,36 @@ def test_packed_reduction_matches_oracle(fmt, sched, M):
     check_linear(fmt, M, N, K, x, w, PACKED[sched])
 
 
+def direct_ok(fmt, c):
+    """Whether a direct-activation schedule exists for the format."""
+    return (fmt != wl.BLOCK_FP8 or c.swap_ab == 1) and (c.reduce == 0 or fmt != wl.BLOCK_FP8)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("name", list(DIRECT))
+@pytest.mark.parametrize("M,K", [(1, 1024), (7, 1040), (32, 2048)])
+def test_direct_activations_match_oracle(fmt, name, M, K):
+    """qlin_gemm and qlin_linear with direct activation loads: every tile
+    shape, ragged K (the last block's bytes past K read as zeros), partial
+    token tiles (rows past M read out of range) and split-K."""
+    c = DIRECT[name]
+    if fmt == wl.BLOCK_FP8 and K % 128:
+        K += 128 - K % 128
+    if not direct_ok(fmt, c):
+        assert q.qlin_validate_config(fmt, M, 512, K, c) == q.QLIN_ERR_INVALID_ARG
+        return
+    N = 512
+    x = wl.activations(fmt, N, K, M) if K % 128 == 0 else wl.random_bf16((M, K), 5)
+    w = wl.random_weights(N, K, 60 + M)
+    check_linear(fmt, M, N, K, x, w, c, "direct")
+    check_layer(fmt, M, N, K, x, w, c)
+
+
+def test_direct_activations_rejected_for_large_m():
+    for fmt in FMTS:
+        assert q.qlin_validate_config(fmt, 64, 512, 1024, cfg(0, 1, 64, 128, 4, 1, act=2)) == q.QLIN_ERR_INVALID_ARG
+
+
 def check_layer(fmt, M, N, K, x, w, c, ldx=None):
     """qlin_linear (quantize + GEMM, fused or not) against the oracle."""
     print(f"[layer] fmt={fmt} M={M} N={N} K={K} cfg={c}", flush=True)
@@ -165,14 +210,14 @@ def check_layer(fmt, M, N, K, x, w, c, ldx=None):
 # the block format) in at most 8 register chunks per thread: 16 rows of
 # K = 1536 need 8 waves.
 LAYER_CFGS = {
-    "fused": cfg(1, 1, 16, 32, 8, 8, fuse=1),
-    "fused_std": cfg(0, 1, 16, 64, 8, 4, fuse=1),
-    "fused_split": cfg(1, 4, 16, 32, 8, 4, fuse=1),
-    "fused_split_std": cfg(0, 3, 16, 16, 8, 8, fuse=1),
-    "fused_nr4": cfg(1, 2, 16, 256, 8, 2, fuse=1),
+    "fused": cfg(1, 1, 16, 32, 8, 8, act=1),
+    "fused_std": cfg(0, 1, 16, 64, 8, 4, act=1),
+    "fused_split": cfg(1, 4, 16, 32, 8, 4, act=1),
+    "fused_split_std": cfg(0, 3, 16, 16, 8, 8, act=1),
+    "fused_nr4": cfg(1, 2, 16, 256, 8, 2, act=1),
     "unfused": cfg(1, 2, 16, 32, 4, 4),
-    "fused_half8": cfg(1, 1, 16, 8, 8, 8, fuse=1),
-    "fused_half16_std_split2": cfg(0, 2, 16, 16, 8, 4, fuse=1),
+    "fused_half8": cfg(1, 1, 16, 8, 8, 8, act=1),
+    "fused_half16_std_split2": cfg(0, 2, 16, 16, 8, 4, act=1),
     "unfused_m32": cfg(0, 2, 32, 64, 4, 2),
 }
 
@@ -192,11 +237,11 @@ def test_linear_fused_few_waves(fmt):
     """In-kernel quantization with 1 and 2 waves (4 and 8 register chunks
     per thread), and the rejection of a tile whose rows do not fit."""
     N, K = 512, 1536
-    for M, c in ((1, cfg(1, 2, 16, 64, 1, 1, fuse=1)), (3, cfg(1, 1, 16, 32, 2, 2, fuse=1))):
+    for M, c in ((1, cfg(1, 2, 16, 64, 1, 1, act=1)), (3, cfg(1, 1, 16, 32, 2, 2, act=1))):
         x = wl.activations(fmt, N, K, M)
         w = wl.random_weights(N, K, 90 + M)
         check_layer(fmt, M, N, K, x, w, c)
-    assert q.qlin_validate_config(fmt, 16, N, K, cfg(1, 2, 16, 64, 1, 1, fuse=1)) == q.QLIN_ERR_INVALID_ARG
+    assert q.qlin_validate_config(fmt, 16, N, K, cfg(1, 2, 16, 64, 1, 1, act=1)) == q.QLIN_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
@@ -209,11 +254,11 @@ def test_linear_fused_packed_stride_and_phases(fmt):
     w = wl.random_weights(N, K, 61)
     red = 1 if fmt != wl.BLOCK_FP8 else 0
     x4 = wl.activations(fmt, N, K, 4)
-    check_layer(fmt, 4, N, K, x4, w, cfg(1, 1, 16, 64, 8, 2, fuse=1), ldx=K + 32)
-    check_layer(fmt, 4, N, K, x4, w, cfg(1, 2, 16, 64, 8, 4, reduce=red, fuse=1), ldx=K + 32)
+    check_layer(fmt, 4, N, K, x4, w, cfg(1, 1, 16, 64, 8, 2, act=1), ldx=K + 32)
+    check_layer(fmt, 4, N, K, x4, w, cfg(1, 2, 16, 64, 8, 4, reduce=red, act=1), ldx=K + 32)
     x16 = wl.activations(fmt, N, K, 16)
     check_layer(fmt, 16, N, K, x16, w, cfg(1, 1, 16, 32, 4, 2), ldx=K + 32)
-    assert q.qlin_validate_config(fmt, 16, N, K, cfg(1, 1, 16, 64, 8, 2, fuse=1)) == q.QLIN_ERR_INVALID_ARG
+    assert q.qlin_validate_config(fmt, 16, N, K, cfg(1, 1, 16, 64, 8, 2, act=1)) == q.QLIN_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
@@ -239,7 +284,7 @@ def test_linear_fused_ragged_k(fmt):
     M, N, K = 5, 256, 1040
     x = wl.random_bf16((M, K), 70)
     w = wl.random_weights(N, K, 71)
-    for c in (cfg(1, 1, 16, 32, 4, 4, fuse=1), cfg(1, 3, 16, 32, 2, 2, reduce=1, fuse=1)):
+    for c in (cfg(1, 1, 16, 32, 4, 4, act=1), cfg(1, 3, 16, 32, 2, 2, reduce=1, act=1)):
         check_layer(fmt, M, N, K, x, w, c)
 
 
@@ -307,11 +352,11 @@ def test_linear_fused_odd_column_waves(fmt):
     two splits, 5 waves hold the whole tile too.)  The largest token count
     each one holds is checked, and the next one is rejected."""
     N, K = 512, 1536
-    for c, ms, too_many in ((cfg(1, 1, 16, 24, 3, 1, fuse=1), (1, 8), 9),
-                            (cfg(0, 2, 16, 40, 5, 1, fuse=1), (2, 13), None if fmt == wl.BLOCK_FP8 else 14),
-                            (cfg(1, 1, 16, 48, 6, 2, fuse=1), (3, 16), None),
-                            (cfg(0, 1, 16, 56, 7, 1, fuse=1), (5, 16), None),
-                            (cfg(1, 3, 16, 224, 7, 1, fuse=1), (1, 23), None)):
+    for c, ms, too_many in ((cfg(1, 1, 16, 24, 3, 1, act=1), (1, 8), 9),
+                            (cfg(0, 2, 16, 40, 5, 1, act=1), (2, 13), None if fmt == wl.BLOCK_FP8 else 14),
+                            (cfg(1, 1, 16, 48, 6, 2, act=1), (3, 16), None),
+                            (cfg(0, 1, 16, 56, 7, 1, act=1), (5, 16), None),
+                            (cfg(1, 3, 16, 224, 7, 1, act=1), (1, 23), None)):
         for M in ms:
             assert q.qlin_validate_config(fmt, M, N, K, c) == 0, (c, M)
             x = wl.activations(fmt, N, K, M)
@@ -381,6 +426,37 @@ def test_quant_act_strided_and_every_bf16(fmt):
     xq, xs = gpu_quant_act(fmt, allv)
     assert np.array_equal(as_u8(xq), qa_o)
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,threads", [(f, t) for f in (wl.FP8_DYNAMIC, wl.W8A8_INT8) for t in (64, 128, 256, 512)]
+                         + [(wl.BLOCK_FP8, 64), (wl.BLOCK_FP8, 256)],
+                         ids=lambda v: str(v))
+def test_quant_act_launch_configs(fmt, threads):
+    """Every launch shape of the quantize kernels gives the oracle's codes
+    and scales: token counts that leave a workgroup's rows partly empty,
+    rows of 1 to 40 chunks per thread (and longer, read twice), a row
+    stride larger than K, and every finite bf16 value."""
+    from _gpu import check_guards, guarded, to_dev_bf16
+    cases = [(1, 1024), (3, 2048), (7, 6144), (33, 4096), (5, 12288), (2, 40960)]
+    if fmt == wl.BLOCK_FP8:
+        cases = [(1, 1024), (3, 2048), (7, 6144), (33, 5120), (5, 25600)]
+    bits = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    allv = bits[np.isfinite(wl.bf16_bits_to_f32(bits))]
+    allv = allv[: (allv.size // 1024) * 1024].reshape(-1, 1024)
+    for M, K in cases + [(allv.shape[0], 1024)]:
+        x = allv if (M, K) == (allv.shape[0], 1024) else wl.activations(fmt, 128, K, M)
+        ldx = K + 64
+        padded = np.zeros((M, ldx), dtype=np.uint16)
+        padded[:, :K] = x
+        xq = guarded((M, K), torch.uint8, 0x55)
+        xs = guarded(q.scales_shape(fmt, M, K, False), torch.float32, -1.0)
+        print(f"[quant-cfg] fmt={fmt} threads={threads} M={M} K={K}", flush=True)
+        q.qlin_quantize_act_cfg(fmt, M, K, to_dev_bf16(padded), ldx, xq, xs, threads)
+        torch.cuda.synchronize()
+        check_guards(xq, xs, what=f"qlin_quantize_act_cfg threads={threads} M={M} K={K}")
+        qa_o, sa_o = oracle.quant_act(fmt, x)
+        assert np.array_equal(as_u8(xq), qa_o), (M, K)
+        assert np.array_equal(xs.cpu().numpy().view(np.uint32), sa_o.view(np.uint32)), (M, K)
 
 
 def test_e4m3_conversion_exhaustive_at_unit_scale():
