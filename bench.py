@@ -585,6 +585,7 @@ def run_workload(name, steps, warmup, detail=False, gemm_only_steps=None, floors
                 kernel_us = per_launch_us(copies, lambda w: l0.kernel(stream, w))
                 del copies
                 rows.append({"layer": l0.name, "M": l0.M, "N": l0.N, "K": l0.K, "fused": l0.fused,
+                             "act_path": ("staged", "fused", "direct")[l0.cfg.act_path],
                              "layer_us": round(layer_us, 3),
                              "layer_GBps": round((l0.bytes + l0.qbytes) / layer_us / 1e3, 1),
                              "layer_TFLOPs": round(l0.flops / layer_us / 1e6, 3),

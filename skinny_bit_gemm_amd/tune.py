@@ -66,24 +66,28 @@ def candidates(fmt, M, N, K):
     nkb = -(-K // 128)
     seen = set()
     out = []
-    tile_m = 16 if M <= 16 else 32
-    for swap in (0, 1):
-        for (tn, waves, kw) in TILES:
-            for split in SPLITS:
-                kbs = -(-nkb // split)
-                eff = -(-nkb // kbs)
-                key = (swap, tn, waves, kw, kbs)
-                if key in seen or kbs < kw:
-                    continue
-                wgs = -(-N // tn) * -(-M // tile_m) * eff
-                if wgs < 16 or wgs > 16384:
-                    continue
-                seen.add(key)
-                acts = (q.QLIN_ACT_STAGED, q.QLIN_ACT_DIRECT) + ((q.QLIN_ACT_FUSED,) if tile_m == 16 else ())
-                for act in acts:
-                    c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, act)
-                    if q.qlin_validate_config(fmt, M, N, K, c) == 0:
-                        out.append(c)
+    # 16-token tiles up to 64 tokens too: two to four token tiles each
+    # re-read the weight tile (from the L2 when they run together), but a
+    # workgroup stages or loads half the activation rows
+    tile_ms = (16,) if M <= 16 else (16, 32) if M <= 64 else (32,)
+    for tile_m in tile_ms:
+        for swap in (0, 1):
+            for (tn, waves, kw) in TILES:
+                for split in SPLITS:
+                    kbs = -(-nkb // split)
+                    eff = -(-nkb // kbs)
+                    key = (tile_m, swap, tn, waves, kw, kbs)
+                    if key in seen or kbs < kw:
+                        continue
+                    wgs = -(-N // tn) * -(-M // tile_m) * eff
+                    if wgs < 16 or wgs > 16384:
+                        continue
+                    seen.add(key)
+                    acts = (q.QLIN_ACT_STAGED, q.QLIN_ACT_DIRECT) + ((q.QLIN_ACT_FUSED,) if tile_m == 16 else ())
+                    for act in acts:
+                        c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, act)
+                        if q.qlin_validate_config(fmt, M, N, K, c) == 0:
+                            out.append(c)
     if M > 32:
         # the large-M kernel: 64- / 128-token tiles of 128 channels
         for tmb in (64, 128):
