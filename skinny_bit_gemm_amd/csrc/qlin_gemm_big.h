@@ -10,15 +10,22 @@
 // here is this one.
 //
 // Work decomposition.  A workgroup of 4 waves owns a BM x 128 tile of the
-// output (tokens x channels) and a range of 128-wide K blocks; the waves
-// form a 2 x 2 grid, each computing (BM/2) x 64 with 16x16x128 fp8 (or
-// 16x16x64 int8) matrix-core instructions on the same lane -> (row, k)
-// fragment assignment as the skinny kernel.
+// output (tokens x channels) and a range of 128-wide K blocks, with
+// 16x16x128 fp8 (or 16x16x64 int8) matrix-core instructions on the same
+// lane -> (row, k) fragment assignment as the skinny kernel.  Two variants:
+//   - staged weights: the waves form a 2 x 2 grid, each computing
+//     (BM/2) x 64, and both operand tiles go through the LDS;
+//   - direct weights (BD): each wave computes all BM tokens x 32 channels
+//     and loads its own weight fragments straight into registers (a ring of
+//     STAGES blocks, refilled in place); only the token tile goes through
+//     the LDS.  A CU's LDS then carries the token fragments only: per
+//     matrix-core instruction, 1.25 KiB of reads and copies instead of 1.5.
 //
-// Operand staging.  Both tiles of a K block are copied by the memory system
-// straight into LDS (buffer loads with the LDS bit: lane l's 16 bytes land
-// 16 l bytes past the wave's LDS address), through a ring of STAGES buffers,
-// STAGES - 1 blocks ahead of the computation, with one barrier per block.
+// Operand staging.  The LDS tiles of a K block are copied by the memory
+// system straight into LDS (buffer loads with the LDS bit: lane l's 16
+// bytes land 16 l bytes past the wave's LDS address), through a ring of
+// STAGES buffers, STAGES - 1 blocks ahead of the computation, with one
+// barrier per block.
 // A tile is stored row by row, 128 bytes per row, 16-byte chunk c of row r
 // at position c ^ (r & 7): one request copies 8 whole rows (1 KB) with a
 // per-lane offset that never changes, and the fragment reads (8 lanes of a
@@ -41,25 +48,39 @@ namespace qlin {
 constexpr int kBigN = 128;         // channels per tile
 constexpr int kBigThreads = 256;   // 4 waves
 
-template <int FMT, int BM>
+// BD (direct weights): the waves split the tile's channels only (each wave
+// all BM tokens x 32 channels) and load their weight fragments straight
+// into registers, a ring of STAGES blocks like the LDS ring; only the
+// token tile goes through the LDS.  Otherwise the waves form a 2 x 2 grid
+// of (BM/2) x 64 and both operand tiles go through the LDS.
+template <int FMT, int BM, bool BD>
 struct BigTile {
-    static constexpr int WM = BM / 2;        // rows per wave
-    static constexpr int FM = WM / 16;       // 16-row fragments per wave
-    static constexpr int FN = 4;             // 16-channel fragments per wave (64 channels)
+    static constexpr int WM = BD ? BM : BM / 2;   // rows per wave
+    static constexpr int FM = WM / 16;            // 16-row fragments per wave
+    static constexpr int FN = BD ? 2 : 4;         // 16-channel fragments per wave
+    static constexpr int WN = 16 * FN;            // channels per wave
     // LDS buffers (blocks in flight: STAGES - 1), sized so that two
     // workgroups share a compute unit: one computes while the other waits
-    static constexpr int STAGES = BM == 64 ? 3 : 2;
+    // (BD: 4, or 2 for the block format's 128-token tiles, whose per-block
+    // scaling leaves registers for two weight slots only)
+    static constexpr int STAGES = BD ? (FMT == FMT_BLOCK && BM == 128 ? 2 : 4) : BM == 64 ? 3 : 2;
     static constexpr int WG_PER_CU = 2;
     static constexpr int A_BYTES = BM * kGroup;
-    static constexpr int B_BYTES = kBigN * kGroup;
+    static constexpr int B_BYTES = BD ? 0 : kBigN * kGroup;
     // block format: token scales of the block (one 64-entry group per wave,
     // entries past BM zero) and the weight block's scale
     static constexpr int S_BYTES = FMT == FMT_BLOCK ? 4 * 64 * 4 + 16 : 0;
     static constexpr int BUF_BYTES = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int REQ_A = BM / 8 / 4;   // 8-row requests per wave and block
-    static constexpr int REQ_B = kBigN / 8 / 4;
+    // weight requests per wave and block: 8-row copies, or (BD) two 16-byte
+    // halves per fragment
+    static constexpr int REQ_B = BD ? 2 * FN : kBigN / 8 / 4;
     static constexpr int REQ = REQ_A + REQ_B + (FMT == FMT_BLOCK ? 2 : 0);
-    static_assert((STAGES - 2) * REQ < 64, "vmcnt holds at most 63");
+    // requests younger than block j's token tile when block j is due: the
+    // younger blocks' (and, BD, one more block of weights, whose ring runs
+    // one block further ahead)
+    static constexpr int WAIT = (STAGES - 2) * REQ + (BD ? REQ_B : 0);
+    static_assert(WAIT < 64, "vmcnt holds at most 63");
     static_assert(STAGES * BUF_BYTES * WG_PER_CU <= 160 * 1024, "LDS of a compute unit");
 };
 
@@ -111,6 +132,20 @@ __device__ __forceinline__ void lds_frags_first_scaled(v4i (&a)[2], v4i (&b)[4][
                      : "memory");
 }
 
+// a token fragment, the lane's 4 token scales of it and the weight block's
+// scale (block format, direct weights)
+__device__ __forceinline__ void lds_frag_scaled(v4i (&a)[2], v4i &sa, float &sw, uint32_t al, uint32_t ah,
+                                                uint32_t sl, uint32_t sb) {
+    asm volatile("ds_read_b128 %[a0l], %[al]\n"
+                 "ds_read_b128 %[a0h], %[ah]\n"
+                 "ds_read_b128 %[s0], %[sl]\n"
+                 "ds_read_b32 %[sw], %[sb]\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : [a0l] "=&v"(a[0]), [a0h] "=&v"(a[1]), [s0] "=&v"(sa), [sw] "=&v"(sw)
+                 : [al] "v"(al), [ah] "v"(ah), [sl] "v"(sl), [sb] "v"(sb)
+                 : "memory");
+}
+
 // one more token fragment
 __device__ __forceinline__ void lds_frag(v4i (&a)[2], uint32_t al, uint32_t ah) {
     asm volatile(QLIN_RD(a0l, al, 0) QLIN_RD(a0h, ah, 0) "s_waitcnt lgkmcnt(0)"
@@ -126,9 +161,9 @@ __device__ __forceinline__ v8i join4(v4i lo, v4i hi) {
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int FMT, int BM>
+template <int FMT, int BM, bool BD>
 __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) {   // two per compute unit
-    typedef BigTile<FMT, BM> T;
+    typedef BigTile<FMT, BM, BD> T;
     typedef typename AccT<FMT>::type acc_t;
     typedef typename AccT<FMT>::scalar acc_s;
     __shared__ __attribute__((aligned(16))) uint8_t lds[T::STAGES * T::BUF_BYTES];
@@ -154,7 +189,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = BD ? 0 : wave & 1, wn = BD ? wave : wave >> 1;
     const int r16 = lane & 15, quarter = lane >> 4;
     const int rows_a = min(BM, M - m0), rows_b = min(kBigN, N - n0);
 
@@ -184,9 +219,10 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     // and 16 lane + 1 KiB of its group.
     typedef __attribute__((address_space(3))) void *lds_ptr;
 
-    // requests of block j of the range into LDS buffer `buf`
-    // (buffers are addressed by their 32-bit LDS addresses)
-    auto issue = [&](int j, uint32_t base) {
+    // requests of block j of the range into LDS buffer `base` (the token
+    // tile, unless BD the weight tile, and the block format's scales;
+    // buffers are addressed by their 32-bit LDS addresses)
+    auto issue_a = [&](int j, uint32_t base) {
         const bool live = j < nsteps;
         const int kb = kb_begin + j;
         const int k0 = kb * kGroup;
@@ -199,24 +235,26 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
                                                      ok ? (uint32_t)(r0 * K) + lane_off : kOutOfRange,
                                                      __builtin_amdgcn_readfirstlane(k0), 0, 0);
         }
+        if constexpr (!BD) {
 #pragma unroll
-        for (int i = 0; i < T::REQ_B; ++i) {
-            const int r0 = (wave * T::REQ_B + i) * 8;
-            if (wpk) {
-                // request j = r0 / 8 is half j % 2 of group j / 2 (the packed
-                // layout holds zeros past K)
-                const int j = r0 >> 3;
-                const bool ok = live && (j >> 1) * kPackRows < rows_b;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
-                    ok ? (uint32_t)lane * 16 : kOutOfRange,
-                    __builtin_amdgcn_readfirstlane(((j >> 1) * g.nkb + kb) * kPackBlock + (j & 1) * (kPackBlock / 2)),
-                    0, 0);
-            } else {
-                const bool ok = kin && r0 + lrow < rows_b;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
-                                                         ok ? (uint32_t)(r0 * K) + lane_off : kOutOfRange,
-                                                         __builtin_amdgcn_readfirstlane(k0), 0, 0);
+            for (int i = 0; i < T::REQ_B; ++i) {
+                const int r0 = (wave * T::REQ_B + i) * 8;
+                if (wpk) {
+                    // request j = r0 / 8 is half j % 2 of group j / 2 (the packed
+                    // layout holds zeros past K)
+                    const int j = r0 >> 3;
+                    const bool ok = live && (j >> 1) * kPackRows < rows_b;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
+                        ok ? (uint32_t)lane * 16 : kOutOfRange,
+                        __builtin_amdgcn_readfirstlane(((j >> 1) * g.nkb + kb) * kPackBlock + (j & 1) * (kPackBlock / 2)),
+                        0, 0);
+                } else {
+                    const bool ok = kin && r0 + lrow < rows_b;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr)(uintptr_t)(base + T::A_BYTES + r0 * kGroup), 16,
+                                                             ok ? (uint32_t)(r0 * K) + lane_off : kOutOfRange,
+                                                             __builtin_amdgcn_readfirstlane(k0), 0, 0);
+                }
             }
         }
         if constexpr (FMT == FMT_BLOCK) {
@@ -231,6 +269,32 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
                                                          live ? (uint32_t)(kb * 4) : kOutOfRange, 0, 0, 0);
         }
     };
+    // direct weights: block j's fragments of the wave's channels into the
+    // register slot `bdst`
+    auto issue_b = [&](int j, v8i (&bdst)[T::FN]) {
+        const bool live = j < nsteps;
+        const int kb = kb_begin + j;
+        const int k0 = kb * kGroup;
+        // the wave's FN fragments of 16 channels straight into registers:
+        // packed, the two 1 KiB halves of the group's block; row-major, the
+        // lane's row, bytes 32 quarter .. + 31 of the block (zeros past K and
+        // past the tile's rows).  One code path for both layouts (offsets
+        // selected, not branched on), so the loads of every slot land in the
+        // same registers.
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn) {
+            const int c0 = wn * T::WN + fn * 16;   // the fragment's first channel in the tile
+            const int kq = k0 + quarter * 32;
+            const uint32_t voff = wpk ? (uint32_t)lane * 16 : (uint32_t)((c0 + r16) * K + quarter * 32);
+            const int soff = __builtin_amdgcn_readfirstlane(wpk ? ((c0 / kPackRows) * g.nkb + kb) * kPackBlock : k0);
+            const int hoff = wpk ? kPackBlock / 2 : 16;
+            const bool lo_ok = live && (wpk ? c0 < rows_b : kq < K);
+            const bool hi_ok = live && (wpk ? c0 < rows_b : kq + 16 < K);
+            const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(brs, lo_ok ? voff : kOutOfRange, soff, 0);
+            const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(brs, hi_ok ? voff : kOutOfRange, soff + hoff, 0);
+            bdst[fn] = join4(lo, hi);
+        }
+    };
 
     acc_t acc[T::FM][T::FN];
 #pragma unroll
@@ -240,25 +304,63 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
 
     // the lane's fragment: row (16-row group base + r16), chunks 2 quarter
     // and 2 quarter + 1, at positions chunk ^ (row & 7); LDS byte addresses
-    const int a_row = wm * T::WM + r16, b_row = wn * 64 + r16;
+    const int a_row = wm * T::WM + r16, b_row = wn * T::WN + r16;
     const int sw = r16 & 7;   // row & 7 (group bases are multiples of 16)
     const uint32_t c_lo = ((2 * quarter) ^ sw) * 16, c_hi = ((2 * quarter + 1) ^ sw) * 16;
     // the lane's weight fragment halves within the B tile: row-major (the
     // swizzled rows), or packed (the wave's first 16-row group, 16 lane and
     // 16 lane + 1 KiB)
-    const uint32_t b_lo = wpk ? (uint32_t)((wn * 64 / kPackRows) * kPackBlock + lane * 16)
+    const uint32_t b_lo = wpk ? (uint32_t)((wn * T::WN / kPackRows) * kPackBlock + lane * 16)
                               : (uint32_t)(b_row * kGroup) + c_lo;
     const uint32_t b_hi = wpk ? b_lo + kPackBlock / 2 : (uint32_t)(b_row * kGroup) + c_hi;
     // one block from the buffer at b0: the channel fragments and the first
     // token fragment, its products, then the requests of a later block
     // (`after`, so that they leave while the matrix core works), then the
     // other token fragments and their products
-    auto compute = [&](uint32_t b0, auto after) {
+    // (direct weights: the channel fragments are the registers `bq`, and
+    // each token fragment is read with its token scales)
+    auto compute = [&](uint32_t b0, const v8i (&bq)[T::FN], auto after) {
         const uint32_t al = b0 + a_row * kGroup + c_lo, ah = b0 + a_row * kGroup + c_hi;
         const uint32_t bl = b0 + T::A_BYTES + b_lo, bh = b0 + T::A_BYTES + b_hi;
         v4i a[2], b[T::FN][2];
         v8i bf[T::FN];
-        if constexpr (FMT == FMT_BLOCK) {
+        if constexpr (BD) {
+            const uint32_t sbase = b0 + T::A_BYTES;
+#pragma unroll
+            for (int fm = 0; fm < T::FM; ++fm) {
+                const uint32_t ao = fm * 16 * kGroup;
+                v8i af;
+                float c[4];
+                if constexpr (FMT == FMT_BLOCK) {
+                    // this block's token scales for the lane's 4 rows, times
+                    // the weight block's scale
+                    v4i sa;
+                    float swt;
+                    lds_frag_scaled(a, sa, swt, al + ao, ah + ao, sbase + (fm * 16 + 4 * quarter) * 4,
+                                    sbase + 4 * 64 * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) c[i] = __int_as_float(sa[i]) * swt;
+                } else {
+                    lds_frag(a, al + ao, ah + ao);
+                }
+                af = join4(a[0], a[1]);
+#pragma unroll
+                for (int fn = 0; fn < T::FN; ++fn) {
+                    if constexpr (FMT == FMT_BLOCK) {
+                        const v4f p4 = block_mma<FMT>(af, bq[fn], v4f{0, 0, 0, 0});
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[fm][fn][i] += p4[i] * c[i];
+                    } else {
+                        acc[fm][fn] = block_mma<FMT>(af, bq[fn], acc[fm][fn]);
+                    }
+                }
+                if (fm == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    after();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else if constexpr (FMT == FMT_BLOCK) {
             v4i sa[T::FM];
             float swt;
             const uint32_t sbase = b0 + T::A_BYTES + T::B_BYTES;
@@ -319,9 +421,19 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     // skipped there.  Unrolled by STAGES, so the buffers' addresses are
     // constants.
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)lds;   // LDS address of the ring
+    // Direct weights: a register ring, slot u holding blocks j = u mod
+    // STAGES, refilled in place (block j + STAGES) once block j's products
+    // are issued, so each slot keeps its registers; the weights run one
+    // block further ahead than the token tiles.  Issue order: B(0), then
+    // A(0) B(1), A(1) B(2), ..., and in pass j A(j + STAGES - 1) then
+    // B(j + STAGES), so that T::WAIT requests are younger than A(j) at
+    // block j on every pass.
+    v8i bq[BD ? T::STAGES : 1][T::FN];
+    if constexpr (BD) issue_b(0, bq[0]);
 #pragma unroll
     for (int st = 0; st < T::STAGES - 1; ++st) {
-        issue(st, lds0 + st * T::BUF_BYTES);
+        issue_a(st, lds0 + st * T::BUF_BYTES);
+        if constexpr (BD) issue_b(st + 1, bq[BD ? st + 1 : 0]);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int j0 = 0; j0 < nsteps; j0 += T::STAGES) {
@@ -329,13 +441,17 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
         for (int u = 0; u < T::STAGES; ++u) {
             const int j = j0 + u;
             const uint32_t next = lds0 + ((u + T::STAGES - 1) % T::STAGES) * T::BUF_BYTES;
-            __builtin_amdgcn_s_waitcnt(vmcnt_only((T::STAGES - 2) * T::REQ));
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(T::WAIT));
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            auto req = [&]() { issue(j + T::STAGES - 1, next); };
-            if (j < nsteps) compute(lds0 + u * T::BUF_BYTES, req);
+            auto req = [&]() { issue_a(j + T::STAGES - 1, next); };
+            if (j < nsteps) compute(lds0 + u * T::BUF_BYTES, bq[BD ? u : 0], req);
             else req();
+            if constexpr (BD) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue_b(j + T::STAGES, bq[BD ? u : 0]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -346,7 +462,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big_kernel(GemmLaunch g) 
     // ---- epilogue.  Lane layout of a 16x16 result: channel r16, tokens
     // 4 * quarter + i.
     const int mrow0 = m0 + wm * T::WM + 4 * quarter;
-    const int ncol0 = n0 + wn * 64 + r16;
+    const int ncol0 = n0 + wn * T::WN + r16;
     auto out_value = [&](acc_s v, int m, int n) -> float {
         if constexpr (FMT == FMT_BLOCK) return (float)v;
         else return ((float)v * g.xs[m]) * g.wsc[n];

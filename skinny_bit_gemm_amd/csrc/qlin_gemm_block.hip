@@ -7,10 +7,13 @@ namespace qlin {
 
 template <bool SWAP>
 static gemm_fn pick(int tile_m, int nr, int xc) {
-    // token tiles of 64 / 128: the large-M kernel (Standard operand roles)
+    // token tiles of 64 / 128: the large-M kernel (Standard operand roles).
+    // Direct weights for 128-token tiles only: with 64-token tiles the block
+    // format's per-fragment scale reads measured 1.4 % slower on geometric
+    // mean than weights staged in the LDS (7.6 % faster with 128-token tiles).
     if (tile_m == 64 || tile_m == 128) {
         if (SWAP || xc != 0) return nullptr;
-        return tile_m == 64 ? gemm_big_kernel<FMT_BLOCK, 64> : gemm_big_kernel<FMT_BLOCK, 128>;
+        return tile_m == 64 ? gemm_big_kernel<FMT_BLOCK, 64, false> : gemm_big_kernel<FMT_BLOCK, 128, true>;
     }
 #define QLIN_PICK(MT_, NR_, XC_) \
     if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_)                                               \

@@ -7,10 +7,11 @@ namespace qlin {
 
 template <bool SWAP>
 static gemm_fn pick(int tile_m, int nr, int xc) {
-    // token tiles of 64 / 128: the large-M kernel (Standard operand roles)
+    // token tiles of 64 / 128: the large-M kernel (Standard operand roles,
+    // weights loaded straight into registers)
     if (tile_m == 64 || tile_m == 128) {
         if (SWAP || xc != 0) return nullptr;
-        return tile_m == 64 ? gemm_big_kernel<FMT_I8, 64> : gemm_big_kernel<FMT_I8, 128>;
+        return tile_m == 64 ? gemm_big_kernel<FMT_I8, 64, true> : gemm_big_kernel<FMT_I8, 128, true>;
     }
 #define QLIN_PICK(MT_, NR_, XC_) \
     if (tile_m == 16 * MT_ && nr == NR_ && xc == XC_)                                               \

@@ -554,3 +554,10 @@ def test_large_m_kernel(fmt, M):
     for c in (cfg(0, 1, 64, 128, 4, 1), cfg(0, 1, 128, 128, 4, 1), cfg(0, 4, 128, 128, 4, 1),
               cfg(0, 2, 64, 128, 4, 1)):
         check_linear(fmt, M, N, K, x, w, c, "large M")
+    if fmt != wl.BLOCK_FP8:
+        # a ragged last K block (K = 1040: 8 blocks and 16 values)
+        K = 1040
+        x = wl.random_bf16((M, K), 130 + M)
+        w = wl.random_weights(N, K, 140 + M)
+        for c in (cfg(0, 1, 64, 128, 4, 1), cfg(0, 3, 128, 128, 4, 1)):
+            check_linear(fmt, M, N, K, x, w, c, "large M, ragged K")
