@@ -70,3 +70,25 @@ def test_headline_is_the_largest_workload_and_the_others_ride_along():
     r = {"step_bytes": 2e9, "ms_step": 1.0, "step_flops": 1e12, "gemm_bytes": 4e9, "ms_gemms": 1.0, "n_gemm": 28}
     s = bench.workload_summary(r)
     assert s["step_GBps"] == 2000.0 and s["gemm_achieved_GBps"] == 4000.0 and s["gemm_frac"] == 0.5
+
+
+def test_table_digest_covers_the_step_buckets_only(tmp_path, monkeypatch):
+    """The traffic record stays valid when only entries of the buckets above
+    32 tokens (which the step never runs) change; any change to an entry the
+    step runs invalidates it."""
+    src = os.path.join(bench.ROOT, bench.TABLE)
+    lines = open(src).read().splitlines(keepends=True)
+    base = tmp_path / "t.tbl"
+    base.write_text("".join(lines))
+    monkeypatch.setattr(bench, "TABLE", str(base))
+    d0 = bench.source_digests()[1]
+    big = next(i for i, l in enumerate(lines) if len(l.split()) == 12 and int(l.split()[3]) > 32)
+    small = next(i for i, l in enumerate(lines) if len(l.split()) == 12 and int(l.split()[3]) <= 32)
+    f = lines[big].split()
+    f[5] = str(int(f[5]) + 1)
+    base.write_text("".join(lines[:big] + [" ".join(f) + "\n"] + lines[big + 1:]))
+    assert bench.source_digests()[1] == d0
+    f = lines[small].split()
+    f[5] = str(int(f[5]) + 1)
+    base.write_text("".join(lines[:small] + [" ".join(f) + "\n"] + lines[small + 1:]))
+    assert bench.source_digests()[1] != d0
