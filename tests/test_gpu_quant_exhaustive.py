@@ -8,13 +8,13 @@ groups for the block format; the rounding rule is the oracle's).  The
 kernels form that quotient from a reciprocal and two residual corrections,
 so they equal the division only if the corrections are right everywhere.
 Activations are bf16, so for one amax the bf16 values x <= amax are the
-whole input domain.  This sweeps all of them, 5.3e8 pairs per format:
+whole input domain.  This sweeps all of them, 5.3e8 magnitude pairs per
+format and sign:
 - per-token formats: one row per amax a, holding every positive bf16 value
   up to a (a is then the row's amax), zero-padded;
-- block format: groups of 128 holding a and up to 127 of the values below it.
-Codes and the fp32 scale bits must equal the oracle's byte for byte.
-Negative values are the same magnitudes with the sign copied: the sweep over
-every finite bf16 value in test_gpu_parity.py covers them.
+- block format: groups of 128 holding a and up to 127 of the values below it;
+and the same rows negated.  Codes and the fp32 scale bits must equal the
+oracle's byte for byte.
 """
 import numpy as np
 import pytest
@@ -55,16 +55,22 @@ def _compare(fmt, bits, what):
                     f"gpu {qg[r, c]:#04x} oracle {qo[r, c]:#04x}")
 
 
+SIGNS = [0, 0x8000]
+SIGN_IDS = ["positive", "negative"]
+
+
+@pytest.mark.parametrize("sign", SIGNS, ids=SIGN_IDS)
 @pytest.mark.parametrize("fmt", [wl.FP8_DYNAMIC, wl.W8A8_INT8], ids=["fp8_dynamic", "w8a8_int8"])
-def test_every_amax_x_pair_per_token(fmt):
+def test_every_amax_x_pair_per_token(fmt, sign):
     col = np.arange(K_TOKEN, dtype=np.int32)[None, :]
     for a0 in range(1, P + 1, ROWS):
         a = np.arange(a0, min(a0 + ROWS, P + 1), dtype=np.int32)[:, None]
-        bits = np.where(col < a, col + 1, 0).astype(np.uint16)   # row r: 1 .. a_r, then zeros
-        _compare(fmt, bits, f"amax bits {a0:#06x}..{int(a[-1, 0]):#06x}")
+        bits = np.where(col < a, (col + 1) | sign, 0).astype(np.uint16)   # row r: +-(1 .. a_r), then zeros
+        _compare(fmt, bits, f"amax bits {a0:#06x}..{int(a[-1, 0]):#06x} sign {sign:#06x}")
 
 
-def test_every_amax_x_pair_block_groups():
+@pytest.mark.parametrize("sign", SIGNS, ids=SIGN_IDS)
+def test_every_amax_x_pair_block_groups(sign):
     fmt = wl.BLOCK_FP8
     G = 128
     per_row = K_TOKEN // G              # groups per row
@@ -76,7 +82,8 @@ def test_every_amax_x_pair_block_groups():
         rows = -(-n // per_row)
         blk = np.zeros((rows * per_row, G), dtype=np.uint16)
         blk[:n] = np.stack(gs)
-        _compare(fmt, blk.reshape(rows, K_TOKEN), f"block groups up to amax bits {int(gs[-1][0]):#06x}")
+        blk[:n] |= np.where(blk[:n] != 0, sign, 0).astype(np.uint16)
+        _compare(fmt, blk.reshape(rows, K_TOKEN), f"block groups up to amax bits {int(gs[-1][0]):#06x} sign {sign:#06x}")
 
     for a in range(1, P + 1):
         xs = np.arange(1, a + 1, dtype=np.uint16)
