@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--moe-layers", default=None, help="layers of --moe (default: all)")
     ap.add_argument("--moe-schedules", default=None,
                     help="schedules of --moe (rule, forced ones, per_expert_launches; default: all)")
+    ap.add_argument("--vendor-sweep", default=None,
+                    help="instead of the step: time hipBLASLt's fp8 GEMM (torch._scaled_mm, reference only) "
+                         "on the crossover sweep's shapes and token counts and write it (JSON) here")
     ap.add_argument("--sweep-formats", default="fp8_dynamic,w8a8_int8,block_fp8")
     ap.add_argument("--sweep-m", default="1,2,4,8,16,24,32,64,128,256,512")
     ap.add_argument("--no-read-ceiling", action="store_true",
@@ -323,6 +326,68 @@ def crossover_sweep(path, fmts, Ms):
     return {"mode": "crossover_sweep", "points": len(rows), "file": path,
             "best_frac_mfma_at_512": {f: max((b["frac_mfma"] for k, b in best.items() if k[0] == f and k[2] == 512),
                                              default=None) for f in sorted({k[0] for k in best})}}
+
+
+def vendor_sweep(path, Ms):
+    """Reference only (no part of the path): hipBLASLt's fp8 GEMM with a
+    scale per token and per channel (torch._scaled_mm, bf16 output) on the
+    8B-class shapes, timed like the crossover sweep (a graph of launches
+    over >= 1 GiB of rotating weight copies).  The same product as the
+    FP8Dynamic GEMM, so it places the large-M kernel against the vendor
+    library on the points where the pages hand the work to one."""
+    import torch
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    rows = []
+    for L in wl.DENSE_8B:
+        N, K = L.N, L.K
+        R = max(2, -(-(1 << 30) // (N * K)))
+        copies = [(torch.randn(N, K, device=dev, generator=gen) * 0.02).to(torch.float8_e4m3fn) for _ in range(R)]
+        sb = torch.rand(1, N, device=dev, generator=gen) * 1e-2 + 1e-3
+        for M in Ms:
+            a = torch.randn(M, K, device=dev, generator=gen).to(torch.float8_e4m3fn)
+            sa = torch.rand(M, 1, device=dev, generator=gen) * 1e-2 + 1e-3
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+
+            def run():
+                for w in copies:
+                    torch._scaled_mm(a, w.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16, out=y)
+            with torch.cuda.stream(st):
+                run()   # the library picks its kernels before the capture
+            torch.cuda.current_stream().wait_stream(st)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run()
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.02:   # ~20 ms untimed, as the other timings
+                g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            del g
+            us = e0.elapsed_time(e1) * 1e3 / (3 * R)
+            tf = wl.flops(M, N, K) / us / 1e6
+            nbytes = wl.algorithmic_bytes(wl.FP8_DYNAMIC, M, N, K)
+            rows.append({"library": "hipBLASLt (torch._scaled_mm, row-wise scales)", "layer": L.name, "N": N,
+                         "K": K, "M": M, "us": round(us, 3), "TFLOPs": round(tf, 2),
+                         "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 4),
+                         "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+            print(f"[vendor] {L.name} M={M}: {us:.2f} us, {tf:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        del copies
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(rows, f, indent=1)
+    return {"mode": "vendor_sweep", "points": len(rows), "file": path}
 
 
 def moe_configs(q, fmt, T):
@@ -725,6 +790,9 @@ def main():
             calibrate_copy(args.calibrate_copy)
         print(json.dumps(moe_bench(args.moe, fmts, Ts, args.moe_layers and args.moe_layers.split(","),
                                    args.moe_schedules and args.moe_schedules.split(","))), flush=True)
+        return
+    if args.vendor_sweep:
+        print(json.dumps(vendor_sweep(args.vendor_sweep, [int(m) for m in args.sweep_m.split(",")])), flush=True)
         return
     if args.sweep:
         fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
