@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--vendor-sweep", default=None,
                     help="instead of the step: time hipBLASLt's fp8 GEMM (torch._scaled_mm, reference only) "
                          "on the crossover sweep's shapes and token counts and write it (JSON) here")
+    ap.add_argument("--vendor-shapes", default="8b",
+                    help="shapes of --vendor-sweep: 8b (the crossover sweep's) or a workload name")
     ap.add_argument("--sweep-formats", default="fp8_dynamic,w8a8_int8,block_fp8")
     ap.add_argument("--sweep-m", default="1,2,4,8,16,24,32,64,128,256,512")
     ap.add_argument("--no-read-ceiling", action="store_true",
@@ -328,7 +330,7 @@ def crossover_sweep(path, fmts, Ms):
                                              default=None) for f in sorted({k[0] for k in best})}}
 
 
-def vendor_sweep(path, Ms):
+def vendor_sweep(path, Ms, shapes="8b"):
     """Reference only (no part of the path): hipBLASLt's fp8 GEMM with a
     scale per token and per channel (torch._scaled_mm, bf16 output) on the
     8B-class shapes, timed like the crossover sweep (a graph of launches
@@ -341,7 +343,9 @@ def vendor_sweep(path, Ms):
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
     rows = []
-    for L in wl.DENSE_8B:
+    # the 8B-class shapes of the crossover sweep, or a workload's layers
+    layers = wl.DENSE_8B if shapes == "8b" else wl.WORKLOADS[shapes][1]
+    for L in layers:
         N, K = L.N, L.K
         R = max(2, -(-(1 << 30) // (N * K)))
         copies = [(torch.randn(N, K, device=dev, generator=gen) * 0.02).to(torch.float8_e4m3fn) for _ in range(R)]
@@ -792,7 +796,8 @@ def main():
                                    args.moe_schedules and args.moe_schedules.split(","))), flush=True)
         return
     if args.vendor_sweep:
-        print(json.dumps(vendor_sweep(args.vendor_sweep, [int(m) for m in args.sweep_m.split(",")])), flush=True)
+        print(json.dumps(vendor_sweep(args.vendor_sweep, [int(m) for m in args.sweep_m.split(",")],
+                                      args.vendor_shapes)), flush=True)
         return
     if args.sweep:
         fmts = [wl.FORMAT_IDS[f] for f in args.sweep_formats.split(",")]
