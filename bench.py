@@ -250,11 +250,15 @@ MFMA_PEAK_TFLOPS = 5000.0   # dense fp8 / int8 matrix-core peak of MI355X
 
 def sweep_configs(q, fmt, M):
     """The forced schedules of the crossover sweep (Standard, Swap-AB,
-    Split-K 2..16, the large-M kernel) and the selection table's pick (None)."""
+    Split-K 2..16, the skinny kernel's 64-token tiles past 32 tokens, the
+    large-M kernel) and the selection table's pick (None)."""
     tm = 16 if M <= 16 else 32
     out = {"standard": q.make_config(0, 1, tm, 64, 4, 2), "swap_ab": q.make_config(1, 1, tm, 64, 4, 2)}
     for sk in (2, 4, 8, 16):
         out[f"splitk{sk}"] = q.make_config(sk % 4 == 0, sk, tm, 64, 4, 2)
+    # the skinny kernel's 64-token tiles (one weight read per 64 tokens)
+    if M > 32:
+        out["skinny64_swap"] = q.make_config(1, 1, 64, 112, 7, 1)
     # the large-M kernel (64- / 128-token tiles), with and without split-K
     for tmb in (64, 128):
         for sk in (1, 2, 4):

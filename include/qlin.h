@@ -96,10 +96,12 @@ typedef enum {
  *   split_k    number of K partitions handled by separate workgroups, 1..64;
  *              each covers ceil(K / split_k) rounded up to 128 (the effective
  *              count can be lower).
- *   tile_m     tokens per tile: 16 or 32 (the skinny kernel), or 64 or 128
- *              (the large-M kernel for token counts past the skinny range:
- *              it needs tile_n 128, waves 4, k_waves 1, swap_ab 0,
- *              reduce 0, act_path 0).
+ *   tile_m     tokens per tile: 16, 32 or 64 (the skinny kernel; 64 with
+ *              codes staged in the LDS only, act_path 0, and 1 or 2
+ *              sub-tiles per wave), or 64 or 128 with tile_n 128, waves 4,
+ *              k_waves 1, swap_ab 0, reduce 0 and act_path 0 (the large-M
+ *              kernel for token counts past the skinny range; 128 takes only
+ *              that layout, and that exact layout with 64 selects it).
  *   tile_n     output channels per workgroup, <= 256: 1, 2 or 4 times
  *              16 x (waves / k_waves) (16-row weight sub-tiles, the matrix
  *              core's), or exactly 8 x (waves / k_waves) (8-row sub-tiles:

@@ -95,12 +95,14 @@ qlin_status make_plan(qlin_format fmt, int M, int N, int K, const qlin_config &c
     const bool fuse = fused && c.act_path == QLIN_ACT_FUSED;
     const bool direct = c.act_path == QLIN_ACT_DIRECT;
     if (c.act_path == QLIN_ACT_FUSED && c.tile_m != 16) return QLIN_ERR_INVALID_ARG;
-    if (direct && c.tile_m >= 64) return QLIN_ERR_INVALID_ARG;
-    if (c.tile_m >= 64) {
-        // The large-M kernel: 128-channel tiles, 4 waves in a 2 x 2 grid,
-        // Standard operand roles, slice reduction, static LDS.
-        if (c.tile_n != 128 || c.waves != 4 || c.k_waves != 1 || c.swap_ab != 0 || c.reduce != 0)
-            return QLIN_ERR_INVALID_ARG;
+    if (direct && c.tile_m >= 64) return QLIN_ERR_INVALID_ARG;   // 16- or 32-token tiles only
+    // The large-M kernel: 64- or 128-token tiles of 128 channels, 4 waves in
+    // a 2 x 2 grid, Standard operand roles, slice reduction, static LDS.  A
+    // 64-token tile with any other layout is the skinny kernel's.
+    const bool big_layout = c.tile_n == 128 && c.waves == 4 && c.k_waves == 1 && c.swap_ab == 0 &&
+                            c.reduce == 0 && c.act_path == QLIN_ACT_STAGED;
+    if (c.tile_m == 128 || (c.tile_m == 64 && big_layout)) {
+        if (!big_layout) return QLIN_ERR_INVALID_ARG;
         if (!gemm_variant_exists(fmt, false, c.tile_m, 0, 0)) return QLIN_ERR_INVALID_ARG;
         p->tile_m = c.tile_m;
         p->tile_n = 128;

@@ -11,7 +11,7 @@ static gemm_fn pick(int tile_m, int nr, int xc) {
     // Direct weights for 128-token tiles only: with 64-token tiles the block
     // format's per-fragment scale reads measured 1.4 % slower on geometric
     // mean than weights staged in the LDS (7.6 % faster with 128-token tiles).
-    if (tile_m == 64 || tile_m == 128) {
+    if ((tile_m == 64 || tile_m == 128) && nr == 0) {
         if (SWAP || xc != 0) return nullptr;
         return tile_m == 64 ? gemm_big_kernel<FMT_BLOCK, 64, false> : gemm_big_kernel<FMT_BLOCK, 128, true>;
     }
@@ -21,6 +21,8 @@ static gemm_fn pick(int tile_m, int nr, int xc) {
                            (XC_ < 0 ? QLIN_PF_DIRECT(QLIN_PF_BLOCK(NR_, XC_), MT_) : QLIN_PF_BLOCK(NR_, XC_)), XC_>;
     QLIN_PICK(1, 1, 0) QLIN_PICK(1, 2, 0) QLIN_PICK(1, 4, 0)
     QLIN_PICK(2, 1, 0) QLIN_PICK(2, 2, 0) QLIN_PICK(2, 4, 0)
+    // 64-token tiles of the skinny kernel (codes staged in the LDS)
+    QLIN_PICK(4, 1, 0) QLIN_PICK(4, 2, 0)
     QLIN_PICK(1, 1, 2) QLIN_PICK(1, 2, 2) QLIN_PICK(1, 4, 2)
     QLIN_PICK(1, 1, 4) QLIN_PICK(1, 2, 4) QLIN_PICK(1, 4, 4)
     QLIN_PICK(1, 1, 8) QLIN_PICK(1, 2, 8) QLIN_PICK(1, 4, 8)

@@ -9,7 +9,7 @@ template <bool SWAP>
 static gemm_fn pick(int tile_m, int nr, int xc) {
     // token tiles of 64 / 128: the large-M kernel (Standard operand roles,
     // weights loaded straight into registers)
-    if (tile_m == 64 || tile_m == 128) {
+    if ((tile_m == 64 || tile_m == 128) && nr == 0) {
         if (SWAP || xc != 0) return nullptr;
         return tile_m == 64 ? gemm_big_kernel<FMT_I8, 64, true> : gemm_big_kernel<FMT_I8, 128, true>;
     }
@@ -19,6 +19,8 @@ static gemm_fn pick(int tile_m, int nr, int xc) {
                            (XC_ < 0 ? QLIN_PF_DIRECT(QLIN_PF(NR_, XC_), MT_) : QLIN_PF(NR_, XC_)), XC_>;
     QLIN_PICK(1, 1, 0) QLIN_PICK(1, 2, 0) QLIN_PICK(1, 4, 0)
     QLIN_PICK(2, 1, 0) QLIN_PICK(2, 2, 0) QLIN_PICK(2, 4, 0)
+    // 64-token tiles of the skinny kernel (codes staged in the LDS)
+    QLIN_PICK(4, 1, 0) QLIN_PICK(4, 2, 0)
     QLIN_PICK(1, 1, 2) QLIN_PICK(1, 2, 2) QLIN_PICK(1, 4, 2)
     QLIN_PICK(1, 1, 4) QLIN_PICK(1, 2, 4) QLIN_PICK(1, 4, 4)
     QLIN_PICK(1, 1, 8) QLIN_PICK(1, 2, 8) QLIN_PICK(1, 4, 8)

@@ -348,8 +348,9 @@ hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, int xc, const Gem
     case FMT_BLOCK: f = gemm_pick_block(swap, tile_m, nr, xc); break;
     }
     if (!f) return hipErrorInvalidValue;
-    if (tile_m >= 64) {
-        // large-M kernel: one-dimensional grid in its XCD-aware tile order
+    if (tile_m >= 64 && nr == 0) {
+        // large-M kernel (nr 0; a 64-token tile with weight sub-tiles is the
+        // skinny kernel's): one-dimensional grid in its XCD-aware tile order
         // (N tiles padded to a multiple of 8), static LDS
         const unsigned n8 = (unsigned)((g.n_tiles + 7) & ~7);
         hipLaunchKernelGGL(f, dim3(n8 * g.m_tiles * g.nsplit), dim3(256), 0, s, g);

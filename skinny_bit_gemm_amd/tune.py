@@ -68,8 +68,9 @@ def candidates(fmt, M, N, K):
     out = []
     # 16-token tiles up to 64 tokens too: two to four token tiles each
     # re-read the weight tile (from the L2 when they run together), but a
-    # workgroup stages or loads half the activation rows
-    tile_ms = (16,) if M <= 16 else (16, 32) if M <= 64 else (32,)
+    # workgroup stages or loads half the activation rows; past 32 tokens
+    # also 64-token tiles, which read each weight tile once per 64 tokens
+    tile_ms = (16,) if M <= 16 else (16, 32) if M <= 32 else (16, 32, 64) if M <= 64 else (32, 64)
     for tile_m in tile_ms:
         for swap in (0, 1):
             for (tn, waves, kw) in TILES:
@@ -86,6 +87,8 @@ def candidates(fmt, M, N, K):
                     acts = (q.QLIN_ACT_STAGED, q.QLIN_ACT_DIRECT) + ((q.QLIN_ACT_FUSED,) if tile_m == 16 else ())
                     for act in acts:
                         c = q.make_config(swap, eff, tile_m, tn, waves, kw, 0, act)
+                        if variant_class(c) == "large_m":
+                            continue   # the large-M kernel's layout: its candidates follow
                         if q.qlin_validate_config(fmt, M, N, K, c) == 0:
                             out.append(c)
     if M > 32:
@@ -208,7 +211,8 @@ class Bench:
 
 
 def variant_class(c):
-    if c.tile_m >= 64:
+    if c.tile_m == 128 or (c.tile_m == 64 and (c.tile_n, c.waves, c.k_waves, c.swap_ab) == (128, 4, 1, 0)
+                           and c.reduce == 0):
         return "large_m"
     if c.split_k > 1:
         return "splitk"

@@ -163,6 +163,20 @@ def test_gemm_rejects_bad_configs():
     for c in (q.make_config(tile_n=8, waves=1, k_waves=1), q.make_config(tile_n=8, waves=4, k_waves=4),
               q.make_config(tile_n=16, waves=2, k_waves=1), q.make_config(tile_n=32, waves=4, k_waves=1)):
         assert q.qlin_validate_config(FP8, 4, 256, 512, c) == OK, c
+    # 64-token tiles: the large-M kernel with its one layout (128 channels,
+    # 4 waves, 1 K wave, Standard roles, slice reduction), the skinny kernel
+    # with any other (staged codes); 128-token tiles are the large-M kernel's
+    for c in (q.make_config(tile_m=64, tile_n=128, waves=4, k_waves=1),
+              q.make_config(tile_m=64, tile_n=32, waves=4, k_waves=4),
+              q.make_config(tile_m=64, swap_ab=1, tile_n=64, waves=2, k_waves=1),
+              q.make_config(tile_m=64, split_k=2, tile_n=128, waves=4, k_waves=1, reduce=1),
+              q.make_config(tile_m=128, tile_n=128, waves=4, k_waves=1)):
+        assert q.qlin_validate_config(FP8, 64, 256, 512, c) == OK, c
+    for c in (q.make_config(tile_m=64, tile_n=256, waves=4, k_waves=1),        # 4 sub-tiles: not built
+              q.make_config(tile_m=64, tile_n=32, waves=4, k_waves=4, act_path=2),
+              q.make_config(tile_m=128, tile_n=64, waves=4, k_waves=1),
+              q.make_config(tile_m=128, swap_ab=1, tile_n=128, waves=4, k_waves=1)):
+        assert q.qlin_validate_config(FP8, 64, 256, 512, c) == EINVAL, c
     # column-wave counts that are not powers of two
     for c in (q.make_config(tile_n=24, waves=3, k_waves=1), q.make_config(tile_n=24, waves=6, k_waves=2),
               q.make_config(tile_n=48, waves=3, k_waves=1), q.make_config(tile_n=96, waves=6, k_waves=2),

@@ -112,13 +112,15 @@ def test_full_size_layers(fmt, layer):
 
 def forced(fmt, M, N, K):
     """Standard, Swap-AB, Split-K 2..16 (both reductions where allowed), the
-    large-M kernel and the table's pick."""
+    skinny kernel's 64-token tiles, the large-M kernel and the table's pick."""
     tm = 32
     out = {"standard": q.make_config(0, 1, tm, 64, 4, 2), "swap_ab": q.make_config(1, 1, tm, 64, 4, 2)}
     for s in (2, 4, 8, 16):
         out[f"splitk{s}"] = q.make_config(s % 4 == 0, s, tm, 64, 4, 2)
     if fmt != wl.BLOCK_FP8:
         out["splitk4_packed"] = q.make_config(1, 4, tm, 64, 8, 4, 1)
+    out["skinny64_swap"] = q.make_config(1, 1, 64, 112, 7, 1)           # 64-token skinny tiles
+    out["skinny64_std_split2"] = q.make_config(0, 2, 64, 64, 8, 4)
     out["large_m128"] = q.make_config(0, 1, 128, 128, 4, 1)
     out["large_m64_split2"] = q.make_config(0, 2, 64, 128, 4, 1)
     out["table"] = None

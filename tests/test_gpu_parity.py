@@ -376,6 +376,37 @@ def test_ragged_n_tiles(fmt):
     check_linear(fmt, M, N, K, x, w, cfg(0, 1, 16, 256, 8, 2))
 
 
+# 64-token tiles of the skinny kernel (four 16-token fragments per weight
+# block; any layout other than the large-M kernel's 128 x 4 x 1 Standard
+# one): at K = 2048 + 16 the 64 staged rows take two to three LDS phases
+SKINNY64 = {
+    "sk64_std": cfg(0, 1, 64, 32, 4, 4),
+    "sk64_swap_nr2_nw2": cfg(1, 1, 64, 64, 2, 1),
+    "sk64_swap_split3": cfg(1, 3, 64, 32, 2, 2),
+    "sk64_half8_swap": cfg(1, 1, 64, 8, 1, 1),
+    "sk64_odd3_std": cfg(0, 1, 64, 48, 3, 1),
+}
+SKINNY64_PACKED = {
+    "sk64_packed2_std": cfg(0, 2, 64, 16, 1, 1, reduce=1),
+    # the large-M kernel's layout but the packed reduction: the skinny kernel
+    "sk64_packed2_big_layout": cfg(0, 2, 64, 128, 4, 1, reduce=1),
+}
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("name", list(SKINNY64) + list(SKINNY64_PACKED))
+@pytest.mark.parametrize("M", [50, 64, 100])
+def test_skinny_64_token_tiles(fmt, name, M):
+    c = SKINNY64.get(name) or SKINNY64_PACKED[name]
+    if name in SKINNY64_PACKED and fmt == wl.BLOCK_FP8:
+        pytest.skip("packed-atomic reduction: exact formats only")
+    N, K = 384, (2048 if fmt == wl.BLOCK_FP8 else 2048 + 16)
+    assert q.qlin_validate_config(fmt, M, N, K, c) == 0, (name, c)
+    x = wl.activations(fmt, N, K, M)
+    w = wl.random_weights(N, K, 100 + M)
+    check_linear(fmt, M, N, K, x, w, c, "64-token skinny tiles")
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("M", [33, 64, 100])
 def test_large_m(fmt, M):
