@@ -33,3 +33,25 @@ def test_table_round_trip_keeps_entries_and_notes(tmp_path):
         assert q.qlin_table_entries() == len(entries)
     finally:
         q.qlin_load_table(q.TABLE_PATH)
+
+
+def test_candidate_grid_token_tiles():
+    """The grid's token tiles per bucket: 16 rows up to 16 tokens, 16 and 32
+    to 32 tokens, the skinny kernel's 64-token tiles joining past 32 tokens
+    and the large-M kernel's layout from 33 tokens on; every candidate is a
+    valid schedule, and only the large-M layout is classed as large-M."""
+    q.lib()
+    fmt, N, K = q.QLIN_FP8_DYNAMIC, 24576, 4096
+
+    def tiles(M):
+        return {(c.tile_m, tune.variant_class(c) == "large_m") for c in tune.candidates(fmt, M, N, K)}
+
+    assert tiles(8) == {(16, False)}
+    assert tiles(32) == {(16, False), (32, False)}
+    assert tiles(64) == {(16, False), (32, False), (64, False), (64, True), (128, True)}
+    assert tiles(256) == {(32, False), (64, False), (64, True), (128, True)}
+    for M in (8, 64, 256):
+        for c in tune.candidates(fmt, M, N, K):
+            assert q.qlin_validate_config(fmt, M, N, K, c) == 0, c
+            if tune.variant_class(c) == "large_m":
+                assert (c.tile_n, c.waves, c.k_waves, c.swap_ab, c.reduce, c.act_path) == (128, 4, 1, 0, 0, 0)
