@@ -141,6 +141,18 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off)
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Cache policy of the weight stream when every weight tile is read by one
+// token tile only (a launch with one tile of tokens, or a grouped launch):
+// non-temporal (the buffer instructions' nt bit).  The weights then pass
+// through once, while the activation codes are read by every workgroup of
+// an XCD; marked non-temporal, the weights no longer push the codes out of
+// the caches.  Measured on the three workload steps: 8 % faster (BlockFP8),
+// 5 % (W8A8INT8 and FP8Dynamic GEMM launches); the sc0 bit alone changed
+// nothing.  With more token tiles the later tiles re-read each weight tile
+// from the caches, and non-temporal weights made those launches 4-6 % slower
+// (crossover sweep, 256 and 512 tokens), so they keep the default policy.
+constexpr int kStreamCpol = 2;
+
 // 32 bytes of the lane's weight row in K block kb: bytes 32 quarter ..
 // 32 quarter + 31 of the block, as two 16-byte halves.  Row-major codes:
 // lane_off = row * K + 32 * quarter in a resource that covers the sub-tile's
@@ -151,15 +163,17 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off)
 // zero.  The block's offset is a scalar operand, so a slot costs no address
 // registers; a dead slot uses an out-of-range lane offset, so every lane
 // issues the same two loads per block and nothing has to be masked after
-// the data arrives.
+// the data arrives.  CPOL: the loads' cache policy (kStreamCpol for
+// weights, 0 for activation fragments, which other waves read too).
+template <int CPOL>
 __device__ __forceinline__ v8i load_w(__amdgpu_buffer_rsrc_t rs, uint32_t lane_off, int kb, int k,
                                       int K, bool live, bool packed) {
     const int boff = __builtin_amdgcn_readfirstlane(kb * (packed ? kPackBlock : kGroup));
     const int hoff = packed ? kPackBlock / 2 : 16;
     const uint32_t lo_off = live && (packed || k < K) ? lane_off : kOutOfRange;
     const uint32_t hi_off = live && (packed || k + 16 < K) ? lane_off : kOutOfRange;
-    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(rs, lo_off, boff, 0);
-    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rs, hi_off, boff + hoff, 0);
+    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(rs, lo_off, boff, CPOL);
+    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rs, hi_off, boff + hoff, CPOL);
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -326,7 +340,8 @@ __device__ __forceinline__ bool group_tile(const int *off, int groups, int total
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int FMT, bool SWAP, int MT, int NR, int PF, int XC>
+// NT: weight loads with the non-temporal cache policy (kStreamCpol)
+template <int FMT, bool SWAP, int MT, int NR, int PF, int XC, bool NT>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
     typedef typename AccT<FMT>::type acc_t;
     typedef typename AccT<FMT>::scalar acc_s;
@@ -476,7 +491,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         const int k = kb * kGroup;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            wbuf[p][r] = load_w(wrs[r], lane_off, kb, k + quarter * 32, K, live, wpk);
+            wbuf[p][r] = load_w<NT ? kStreamCpol : 0>(wrs[r], lane_off, kb, k + quarter * 32, K, live, wpk);
             if constexpr (FMT == FMT_BLOCK) {
                 const int soff = __builtin_amdgcn_readfirstlane(
                     ((min(nsub[r], N - 1) / kGroup) * G + min(kb, G - 1)) * 4);
@@ -486,7 +501,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemm_kernel(GemmLaunch g) {
         if constexpr (DIRECT) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                abuf[p][mt] = load_w(ars, a_off[mt], kb, k + quarter * 32, K, live, false);
+                abuf[p][mt] = load_w<0>(ars, a_off[mt], kb, k + quarter * 32, K, live, false);
                 if constexpr (FMT == FMT_BLOCK)
                     asbuf[p][mt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                         asr, live ? (uint32_t)(((mt * 16 + r16) * G + kb) * 4) : kOutOfRange, 0, 0));
@@ -969,9 +984,10 @@ typedef void (*gemm_fn)(GemmLaunch);
 
 // The kernel for a (format, schedule, tile) choice, or null; defined by the
 // per-format source files.  xc: register chunks of the in-kernel
-// quantization (0 = codes come quantized).
-gemm_fn gemm_pick_fp8(bool swap, int tile_m, int nr, int xc);
-gemm_fn gemm_pick_i8(bool swap, int tile_m, int nr, int xc);
-gemm_fn gemm_pick_block(bool swap, int tile_m, int nr, int xc);
+// quantization (0 = codes come quantized); nt: the skinny kernel's weights
+// with the non-temporal cache policy.
+gemm_fn gemm_pick_fp8(bool swap, int tile_m, int nr, int xc, bool nt);
+gemm_fn gemm_pick_i8(bool swap, int tile_m, int nr, int xc, bool nt);
+gemm_fn gemm_pick_block(bool swap, int tile_m, int nr, int xc, bool nt);
 
 }  // namespace qlin

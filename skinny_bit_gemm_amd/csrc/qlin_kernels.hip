@@ -332,20 +332,24 @@ hipError_t static_scratch(hipStream_t s, void **out) {
 
 bool gemm_variant_exists(int fmt, bool swap, int tile_m, int nr, int xc) {
     switch (fmt) {
-    case FMT_FP8: return gemm_pick_fp8(swap, tile_m, nr, xc) != nullptr;
-    case FMT_I8: return gemm_pick_i8(swap, tile_m, nr, xc) != nullptr;
-    case FMT_BLOCK: return gemm_pick_block(swap, tile_m, nr, xc) != nullptr;
+    case FMT_FP8: return gemm_pick_fp8(swap, tile_m, nr, xc, false) != nullptr;
+    case FMT_I8: return gemm_pick_i8(swap, tile_m, nr, xc, false) != nullptr;
+    case FMT_BLOCK: return gemm_pick_block(swap, tile_m, nr, xc, false) != nullptr;
     }
     return false;
 }
 
 hipError_t launch_gemm(int fmt, bool swap, int tile_m, int nr, int xc, const GemmLaunch &g,
                        size_t lds_bytes, hipStream_t s) {
+    // the skinny kernel streams its weights with the non-temporal policy when
+    // each weight tile is read by one token tile: one tile of tokens, or a
+    // grouped launch (each expert's rows are normally one tile)
+    const bool nt = g.group_off != nullptr || g.m_tiles == 1;
     gemm_fn f = nullptr;
     switch (fmt) {
-    case FMT_FP8: f = gemm_pick_fp8(swap, tile_m, nr, xc); break;
-    case FMT_I8: f = gemm_pick_i8(swap, tile_m, nr, xc); break;
-    case FMT_BLOCK: f = gemm_pick_block(swap, tile_m, nr, xc); break;
+    case FMT_FP8: f = gemm_pick_fp8(swap, tile_m, nr, xc, nt); break;
+    case FMT_I8: f = gemm_pick_i8(swap, tile_m, nr, xc, nt); break;
+    case FMT_BLOCK: f = gemm_pick_block(swap, tile_m, nr, xc, nt); break;
     }
     if (!f) return hipErrorInvalidValue;
     if (tile_m >= 64 && nr == 0) {
